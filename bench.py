@@ -1,0 +1,257 @@
+"""Benchmark of the block-scaled FP8 GEMM on one MI355X.
+
+One step = one launch of the GEMM (the whole path: host validation, operand
+and scale fetch, MFMA partials, per-K-block promotion, bf16 epilogue) over one
+batch of synthetic inputs already resident in HBM. The headline workload is
+the decode-shaped dense GEMM M=8, N=4096, K=7168, which is bound by streaming
+B from HBM; its metric is HBM GB/s of algorithmic bytes (A + sA + B + sB + D,
+each counted once). The other workloads are timed the same way and reported
+under "workloads".
+
+Memory-bound workloads rotate over enough copies of their operands (> 2x the
+256 MB last-level cache) that every launch reads its B from HBM.
+
+Prints ONE JSON line on stdout.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
+FP8_PEAK_TFLOPS = 5000.0       # MI355X dense FP8 MFMA, published (no sparsity)
+ROTATE_BYTES = 600 * 2 ** 20   # > 2x the 256 MB last-level cache
+HEADLINE = "decode_8x4096x7168"
+METRIC = "FP8 GEMM TFLOP/s (and HBM GB/s at small M) + % of MI355X roofline, 1 GPU"
+KERNEL_SOURCES = ["fp8_block_scaled_sa_amd/csrc/kernels.hpp", "fp8_block_scaled_sa_amd/csrc/dg_fp8.hip"]
+
+
+def kernel_hash() -> str:
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def work(name, p):
+    """Algorithmic flops and bytes (each tensor read or written once, real rows only)."""
+    from synth import gen
+    kind = gen.CONFIGS[name]["kind"]
+    if kind == "dense":
+        M, N, K = p.M, p.N, p.K
+        flops = 2 * M * N * K
+        byts = M * K + M * (K // 128) * 4 + N * K + (N // 128) * (K // 128) * 4 + M * N * 2
+        return flops, byts, M
+    if kind == "contiguous":
+        N, K = p.N, p.K
+        rows = int((p.ids >= 0).sum())
+        used = int((p.counts > 0).sum())
+        flops = 2 * rows * N * K
+        byts = (p.M_total * K + p.M_total * (K // 128) * 4 + used * (N * K + (N // 128) * (K // 128) * 4)
+                + rows * N * 2 + p.M_total * 4)
+        return flops, byts, rows
+    N, K = p.N, p.K
+    rows = int(np.clip(p.masked_m, 0, p.M_max).sum())
+    used = int((p.masked_m > 0).sum())
+    flops = 2 * rows * N * K
+    byts = (rows * K + rows * (K // 128) * 4 + used * (N * K + (N // 128) * (K // 128) * 4)
+            + rows * N * 2 + p.G * 4)
+    return flops, byts, rows
+
+
+class Launcher:
+    """Device copies of one workload and a closure that launches copy i."""
+
+    def __init__(self, name, p, rotate):
+        import torch
+        from fp8_block_scaled_sa_amd import ops
+        from synth import gen
+        self.kind = gen.CONFIGS[name]["kind"]
+        dev = torch.device("cuda:0")
+        t = lambda x: torch.from_numpy(np.ascontiguousarray(x)).to(dev)  # noqa: E731
+        self.copies = []
+        if self.kind == "dense":
+            one = p.a.nbytes + p.b.nbytes
+            n = max(1, min(64, -(-ROTATE_BYTES // one))) if rotate else 1
+            a, sa, b, sb = t(p.a), t(p.sa_t), t(p.b), t(p.sb)
+            d = torch.empty((p.M, p.N), dtype=torch.bfloat16, device=dev)
+            for i in range(n):
+                c = (a, sa, b, sb) if i == 0 else (a.clone(), sa.clone(), b.clone(), sb.clone())
+                self.copies.append(c)
+            self.fn = lambda c: ops.dg_fp8_gemm_nt(c[0], c[1].t(), c[2], c[3], d=d)
+        elif self.kind == "contiguous":
+            one = p.a.nbytes + p.b.nbytes
+            n = max(1, min(8, -(-ROTATE_BYTES // one))) if rotate else 1
+            base = (t(p.a), t(p.sa_t), t(p.b), t(p.sb), t(p.ids))
+            d = torch.empty((p.M_total, p.N), dtype=torch.bfloat16, device=dev)
+            for i in range(n):
+                self.copies.append(base if i == 0 else tuple(x.clone() for x in base))
+            self.fn = lambda c: ops.dg_fp8_grouped_gemm_contiguous(c[0], c[1].t(), c[2], c[3], c[4], d=d)
+        else:
+            one = p.a.nbytes + p.b.nbytes
+            n = max(1, min(8, -(-ROTATE_BYTES // one))) if rotate else 1
+            base = (t(p.a), t(p.sa_t), t(p.b), t(p.sb), t(p.masked_m))
+            d = torch.empty((p.G, p.M_max, p.N), dtype=torch.bfloat16, device=dev)
+            for i in range(n):
+                self.copies.append(base if i == 0 else tuple(x.clone() for x in base))
+            self.fn = lambda c: ops.dg_fp8_grouped_gemm_masked(c[0], c[1].transpose(1, 2), c[2], c[3], c[4], d=d)
+
+    def __call__(self, i):
+        self.fn(self.copies[i % len(self.copies)])
+
+
+def time_workload(name, steps, warmup, rotate=True):
+    """Warm up eagerly, then time exactly `steps` launches captured in one HIP
+    graph (so host launch overhead is not measured), with HIP events on the
+    stream the kernels run on around the replay. Eager per-launch events are
+    kept as a cross-check."""
+    import torch
+    from synth import gen
+    p = gen.make_config(name)
+    flops, byts, rows = work(name, p)
+    run = Launcher(name, p, rotate)
+    for i in range(warmup):
+        run(i)
+    torch.cuda.synchronize()
+
+    # eager cross-check: one event pair per launch
+    cur = torch.cuda.current_stream()
+    n_eager = min(steps, 50)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n_eager)]
+    for i in range(n_eager):
+        ev[i][0].record(cur)
+        run(i)
+        ev[i][1].record(cur)
+    torch.cuda.synchronize()
+    eager_us = [a.elapsed_time(b) * 1e3 for a, b in ev]
+
+    # the timed region: `steps` launches in one graph
+    graph = torch.cuda.CUDAGraph()
+    cap = torch.cuda.Stream()
+    cap.wait_stream(cur)
+    with torch.cuda.graph(graph, stream=cap):
+        for i in range(steps):
+            run(warmup + i)
+    graph.replay()                  # untimed: first replay uploads the graph
+    torch.cuda.synchronize()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    start.record(cap)
+    with torch.cuda.stream(cap):
+        graph.replay()
+    end.record(cap)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    avg_kernel_s = start.elapsed_time(end) / 1e3 / steps
+    del graph
+    return dict(p=p, flops=flops, bytes=byts, rows=rows, copies=len(run.copies),
+                wall_s=wall, ms_per_step=wall / steps * 1e3,
+                kernel_avg_us=avg_kernel_s * 1e6,
+                eager_med_us=float(np.median(eager_us)), eager_min_us=float(np.min(eager_us)),
+                tflops=flops / avg_kernel_s / 1e12, gbs=byts / avg_kernel_s / 1e9)
+
+
+def cpu_baseline(name, p, byts):
+    """The oracle, as it stands, on this host's cores, over the full workload."""
+    import oracle
+    threads = min(16, len(os.sched_getaffinity(0)))   # the GPU machine grants 16 cores per GPU
+    t0 = time.perf_counter()
+    oracle.gemm_nt(p.a, p.sa_t.T, p.b, p.sb, threads=threads)
+    dt = time.perf_counter() - t0
+    return {"value": round(byts / dt / 1e9, 4), "unit": "GB/s", "cores": threads, "kind": "oracle",
+            "sample": "the full %s problem (all %d outputs), one pass, %.2f s" % (name, p.M * p.N, dt)}
+
+
+def load_traffic(kernel_name):
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        tr = json.load(f)
+    ent = tr.get(kernel_name)
+    if not ent or ent.get("kernel_hash") != kernel_hash():
+        return None
+    return ent.get("bytes_per_launch")
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default=HEADLINE)
+    ap.add_argument("--others", default="all",
+                    help="comma-separated extra workloads to time, 'all' or 'none'")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(--gpus %d requested)" % args.gpus, file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from synth import gen
+    assert torch.cuda.is_available(), "needs a GPU"
+
+    head = time_workload(args.workload, args.steps, args.warmup)
+    p = head["p"]
+    traffic = load_traffic(args.workload)
+    kind = gen.CONFIGS[args.workload]["kind"]
+    small_m = kind == "dense" and p.M <= 64
+    if small_m:
+        value, unit = head["bytes"] / (head["ms_per_step"] / 1e3) / 1e9, "GB/s"
+        roof = {"bound": "hbm", "achieved": round(head["gbs"], 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(head["gbs"] / HBM_PEAK_GBS, 4), "traffic": traffic}
+    else:
+        value, unit = head["flops"] / (head["ms_per_step"] / 1e3) / 1e12, "TFLOP/s"
+        roof = {"bound": "mfma", "achieved": round(head["tflops"], 2), "peak": FP8_PEAK_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(head["tflops"] / FP8_PEAK_TFLOPS, 4), "traffic": traffic}
+    roof["kernel_avg_us"] = round(head["kernel_avg_us"], 3)
+    roof["eager_launch_med_us"] = round(head["eager_med_us"], 3)
+    roof["algorithmic_bytes"] = head["bytes"]
+    roof["algorithmic_flops"] = head["flops"]
+
+    others = {}
+    names = [] if args.others == "none" else (
+        [n for n in gen.CONFIGS if n != args.workload] if args.others == "all" else args.others.split(","))
+    for n in names:
+        r = time_workload(n, max(10, args.steps // 10), max(3, args.warmup // 4))
+        others[n] = {"kernel_avg_us": round(r["kernel_avg_us"], 2), "eager_med_us": round(r["eager_med_us"], 2),
+                     "tflops": round(r["tflops"], 2), "gbs": round(r["gbs"], 1),
+                     "frac_fp8_peak": round(r["tflops"] / FP8_PEAK_TFLOPS, 4),
+                     "frac_hbm_peak": round(r["gbs"] / HBM_PEAK_GBS, 4), "rows": r["rows"],
+                     "operand_copies": r["copies"]}
+        del r
+        torch.cuda.empty_cache()
+
+    cpu = None if args.no_cpu_baseline or kind != "dense" else cpu_baseline(args.workload, p, head["bytes"])
+
+    line = {
+        "metric": METRIC, "value": round(value, 3), "unit": unit, "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(head["ms_per_step"], 6),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "fp8_e4m3 (fp32 accumulate, bf16 out)", "data": "synthetic",
+        "config": {"workload": args.workload, "M": p.M, "N": p.N, "K": p.K,
+                   "lhs_scale": "1x128", "rhs_scale": "128x128", "operand_copies": head["copies"]},
+        "tflops": round(head["tflops"], 3),
+        "roofline": roof,
+        "cpu_baseline": cpu,
+        "workloads": others,
+        "kernel_hash": kernel_hash(),
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

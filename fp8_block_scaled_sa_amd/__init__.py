@@ -1,0 +1,9 @@
+"""MI355X (gfx950) fine-grained block-scaled FP8 GEMM.
+
+D = A . B^T with e4m3 operands, 1x128 LHS scales, 128x128 RHS scales, fp32
+per-K-block promotion and a bf16 output, as a dense NT GEMM and as two MoE
+grouped layouts (contiguous, masked). The kernels live in libdg_fp8.so behind
+the C ABI of include/dg_fp8.h; this package is its thin Python binding.
+"""
+from .ops import (DGError, dg_fp8_gemm_nt, dg_fp8_grouped_gemm_contiguous,  # noqa: F401
+                  dg_fp8_grouped_gemm_masked)

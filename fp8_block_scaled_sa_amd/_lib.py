@@ -1,0 +1,48 @@
+"""ctypes loader of libdg_fp8.so. Fails loudly when the library is missing."""
+from __future__ import annotations
+
+import ctypes
+import os
+
+from . import build as _build
+
+_i64 = ctypes.c_int64
+_p = ctypes.c_void_p
+
+# Entry points declared in include/dg_fp8.h, with their argument types.
+SIGNATURES = {
+    "dg_abi_version": (ctypes.c_int, []),
+    "dg_status_string": (ctypes.c_char_p, [ctypes.c_int]),
+    "dg_last_hip_error": (ctypes.c_int, []),
+    "dg_fp8_gemm_nt": (ctypes.c_int, [_p, _i64, _p, _i64, _i64, _p, _i64, _p, _i64, _i64,
+                                      _p, _i64, _i64, _i64, _i64, _p]),
+    "dg_fp8_grouped_gemm_contiguous": (ctypes.c_int, [_p, _i64, _p, _i64, _i64, _p, _i64, _i64,
+                                                      _p, _i64, _i64, _i64, _p, _p, _i64,
+                                                      _i64, _i64, _i64, _i64, _p]),
+    "dg_fp8_grouped_gemm_masked": (ctypes.c_int, [_p, _i64, _i64, _p, _i64, _i64, _i64,
+                                                  _p, _i64, _i64, _p, _i64, _i64, _i64, _p,
+                                                  _p, _i64, _i64, _i64, _i64, _i64, _i64, _p]),
+}
+
+_lib = None
+
+
+def path() -> str:
+    return _build.LIBRARY
+
+
+def load() -> ctypes.CDLL:
+    """Load the HIP library (built beforehand by __graft_entry__.build())."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_build.LIBRARY):
+            raise ImportError(
+                "libdg_fp8.so is not built (expected at %s); run "
+                "`python -c 'import __graft_entry__ as g; g.build()'` first" % _build.LIBRARY)
+        lib = ctypes.CDLL(_build.LIBRARY)
+        for name, (res, args) in SIGNATURES.items():
+            fn = getattr(lib, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = lib
+    return _lib

@@ -1,0 +1,289 @@
+// dg_fp8.hip -- C ABI of the gfx950 block-scaled FP8 GEMM (declared in
+// include/dg_fp8.h): host-side validation, device check, kernel choice and
+// launch. No device memory is allocated and no stream is synchronised.
+#include <hip/hip_runtime.h>
+
+#include <mutex>
+#include <stdint.h>
+#include <string.h>
+
+#include "dg_fp8.h"
+#include "kernels.hpp"
+
+namespace {
+
+thread_local int g_last_hip_error = 0;
+
+struct DeviceInfo {
+    bool known = false;
+    bool gfx950 = false;
+    int cus = 0;
+};
+
+constexpr int kMaxDevices = 64;
+DeviceInfo g_devices[kMaxDevices];
+std::mutex g_devices_mu;
+
+int fail_hip(hipError_t e)
+{
+    g_last_hip_error = (int)e;
+    return DG_ERR_HIP;
+}
+
+// Checks that the current device is gfx950 and caches its CU count.
+int current_device(DeviceInfo &out)
+{
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess)
+        return fail_hip(e);
+    if (dev < 0 || dev >= kMaxDevices)
+        return DG_ERR_UNSUPPORTED;
+    std::lock_guard<std::mutex> lk(g_devices_mu);
+    DeviceInfo &d = g_devices[dev];
+    if (!d.known) {
+        hipDeviceProp_t prop;
+        e = hipGetDeviceProperties(&prop, dev);
+        if (e != hipSuccess)
+            return fail_hip(e);
+        d.gfx950 = strncmp(prop.gcnArchName, "gfx950", 6) == 0;
+        d.cus = prop.multiProcessorCount;
+        d.known = true;
+    }
+    out = d;
+    return d.gfx950 ? DG_OK : DG_ERR_UNSUPPORTED;
+}
+
+bool aligned(const void *p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
+
+// [lo, hi) byte extent of a strided 2-D/3-D operand (all strides >= 0).
+struct Extent {
+    uintptr_t lo, hi;
+};
+
+Extent extent(const void *p, int64_t elem, int64_t last_index)
+{
+    const uintptr_t lo = (uintptr_t)p;
+    return Extent{lo, lo + (uintptr_t)((last_index + 1) * elem)};
+}
+
+bool overlaps(Extent a, Extent b) { return a.lo < b.hi && b.lo < a.hi; }
+
+constexpr int64_t kInt32Max = 0x7fffffff;
+
+int check_common_shape(int64_t M, int64_t N, int64_t K)
+{
+    if (M < 0 || N < 0 || K <= 0)
+        return DG_ERR_BAD_SHAPE;
+    if (K % 128 != 0 || N % 128 != 0)
+        return DG_ERR_BAD_SHAPE;
+    if (M > kInt32Max || N > kInt32Max || K > kInt32Max)
+        return DG_ERR_UNSUPPORTED;
+    return DG_OK;
+}
+
+// sA extent for rows [0, rows) and nkb K blocks.
+int64_t last_scale_index(int64_t rows, int64_t nkb, int64_t s_row, int64_t s_kb)
+{
+    return (rows - 1) * s_row + (nkb - 1) * s_kb;
+}
+
+template <typename Kern>
+int launch(Kern kernel, int grid, hipStream_t stream, const dgk::Params &p)
+{
+    hipLaunchKernelGGL(kernel, dim3(grid), dim3(dgk::kThreads), 0, stream, p);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess)
+        return fail_hip(e);
+    return DG_OK;
+}
+
+// Workgroups resident per CU for the tile kernels (LDS and registers allow 2).
+constexpr int kTileOccupancy = 2;
+
+template <int L, int BM, int BN>
+int launch_tiles(dgk::Params &p, int groups, int cus, hipStream_t stream)
+{
+    p.tiles_m = (int)((p.M + BM - 1) / BM);
+    p.tiles_n = p.N / BN;
+    const int64_t tiles = (int64_t)p.tiles_m * p.tiles_n * groups;
+    if (tiles > kInt32Max)
+        return DG_ERR_UNSUPPORTED;
+    p.num_tiles = (int)tiles;
+    if (p.num_tiles == 0)
+        return DG_OK;
+    int grid = cus * kTileOccupancy;
+    if (p.num_tiles < grid)
+        grid = p.num_tiles;
+    return launch(dgk::tile_kernel<L, BM, BN>, grid, stream, p);
+}
+
+int launch_decode(dgk::Params &p, hipStream_t stream)
+{
+    const int grid = p.N / 16;
+    if (p.M <= 16)
+        return launch(dgk::decode_kernel<1>, grid, stream, p);
+    if (p.M <= 32)
+        return launch(dgk::decode_kernel<2>, grid, stream, p);
+    return launch(dgk::decode_kernel<4>, grid, stream, p);
+}
+
+}  // namespace
+
+extern "C" {
+
+int dg_abi_version(void) { return DG_ABI_VERSION; }
+
+const char *dg_status_string(int status)
+{
+    switch (status) {
+    case DG_OK: return "ok";
+    case DG_ERR_NULL_POINTER: return "a required pointer is NULL";
+    case DG_ERR_BAD_SHAPE: return "bad shape (need K > 0, K % 128 == 0, N % 128 == 0, M_total % 128 == 0, dims >= 0)";
+    case DG_ERR_MISALIGNED: return "misaligned pointer or stride (16-byte operands/strides, 4-byte scales)";
+    case DG_ERR_BAD_STRIDE: return "bad stride (lda/ldb >= K, ldd >= N, non-negative, group strides cover a group)";
+    case DG_ERR_UNSUPPORTED: return "unsupported device (gfx950 required) or size beyond int32";
+    case DG_ERR_HIP: return "HIP runtime error (see dg_last_hip_error)";
+    case DG_ERR_ALIASING: return "output overlaps an input";
+    default: return "unknown status";
+    }
+}
+
+int dg_last_hip_error(void) { return g_last_hip_error; }
+
+int dg_fp8_gemm_nt(const void *A, int64_t lda, const float *sA, int64_t sa_stride_m, int64_t sa_stride_kb,
+                   const void *B, int64_t ldb, const float *sB, int64_t sb_stride_nb, int64_t sb_stride_kb,
+                   void *D, int64_t ldd, int64_t M, int64_t N, int64_t K, void *stream)
+{
+    int st = check_common_shape(M, N, K);
+    if (st != DG_OK)
+        return st;
+    if (M == 0 || N == 0)
+        return DG_OK;
+    if (!A || !sA || !B || !sB || !D)
+        return DG_ERR_NULL_POINTER;
+    if (lda < K || ldb < K || ldd < N || sa_stride_m < 0 || sa_stride_kb < 0 || sb_stride_nb < 0 ||
+        sb_stride_kb < 0)
+        return DG_ERR_BAD_STRIDE;
+    if (!aligned(A, 16) || !aligned(B, 16) || !aligned(D, 16) || lda % 16 || ldb % 16 || ldd % 8 ||
+        !aligned(sA, 4) || !aligned(sB, 4))
+        return DG_ERR_MISALIGNED;
+    const int64_t nkb = K / 128;
+    const Extent ed = extent(D, 2, (M - 1) * ldd + N - 1);
+    if (overlaps(ed, extent(A, 1, (M - 1) * lda + K - 1)) || overlaps(ed, extent(B, 1, (N - 1) * ldb + K - 1)) ||
+        overlaps(ed, extent(sA, 4, last_scale_index(M, nkb, sa_stride_m, sa_stride_kb))) ||
+        overlaps(ed, extent(sB, 4, last_scale_index(N / 128, nkb, sb_stride_nb, sb_stride_kb))))
+        return DG_ERR_ALIASING;
+    DeviceInfo dev;
+    if ((st = current_device(dev)) != DG_OK)
+        return st;
+
+    dgk::Params p = {};
+    p.A = (const uint8_t *)A; p.lda = lda;
+    p.sA = sA; p.sa_m = sa_stride_m; p.sa_kb = sa_stride_kb;
+    p.B = (const uint8_t *)B; p.ldb = ldb;
+    p.sB = sB; p.sb_nb = sb_stride_nb; p.sb_kb = sb_stride_kb;
+    p.D = (uint16_t *)D; p.ldd = ldd;
+    p.M = (int)M; p.N = (int)N; p.K = (int)K; p.G = 1;
+    hipStream_t s = (hipStream_t)stream;
+    if (M <= 64)
+        return launch_decode(p, s);
+    return launch_tiles<dgk::kDense, 128, 128>(p, 1, dev.cus, s);
+}
+
+int dg_fp8_grouped_gemm_contiguous(const void *A, int64_t lda, const float *sA, int64_t sa_stride_m,
+                                   int64_t sa_stride_kb, const void *B, int64_t ldb, int64_t b_stride_g,
+                                   const float *sB, int64_t sb_stride_g, int64_t sb_stride_nb, int64_t sb_stride_kb,
+                                   const int32_t *expert_ids, void *D, int64_t ldd, int64_t M_total, int64_t N,
+                                   int64_t K, int64_t G, void *stream)
+{
+    int st = check_common_shape(M_total, N, K);
+    if (st != DG_OK)
+        return st;
+    if (G < 0 || M_total % 128 != 0)
+        return DG_ERR_BAD_SHAPE;
+    if (G > kInt32Max)
+        return DG_ERR_UNSUPPORTED;
+    if (M_total == 0 || N == 0 || G == 0)
+        return DG_OK;
+    if (!A || !sA || !B || !sB || !expert_ids || !D)
+        return DG_ERR_NULL_POINTER;
+    if (lda < K || ldb < K || ldd < N || sa_stride_m < 0 || sa_stride_kb < 0 || sb_stride_nb < 0 ||
+        sb_stride_kb < 0 || sb_stride_g < 0 || (G > 1 && b_stride_g < (N - 1) * ldb + K))
+        return DG_ERR_BAD_STRIDE;
+    if (!aligned(A, 16) || !aligned(B, 16) || !aligned(D, 16) || lda % 16 || ldb % 16 || b_stride_g % 16 ||
+        ldd % 8 || !aligned(sA, 4) || !aligned(sB, 4) || !aligned(expert_ids, 4))
+        return DG_ERR_MISALIGNED;
+    const int64_t nkb = K / 128;
+    const Extent ed = extent(D, 2, (M_total - 1) * ldd + N - 1);
+    if (overlaps(ed, extent(A, 1, (M_total - 1) * lda + K - 1)) ||
+        overlaps(ed, extent(B, 1, (G - 1) * b_stride_g + (N - 1) * ldb + K - 1)) ||
+        overlaps(ed, extent(sA, 4, last_scale_index(M_total, nkb, sa_stride_m, sa_stride_kb))) ||
+        overlaps(ed, extent(sB, 4, (G - 1) * sb_stride_g + last_scale_index(N / 128, nkb, sb_stride_nb, sb_stride_kb))) ||
+        overlaps(ed, extent(expert_ids, 4, M_total - 1)))
+        return DG_ERR_ALIASING;
+    DeviceInfo dev;
+    if ((st = current_device(dev)) != DG_OK)
+        return st;
+
+    dgk::Params p = {};
+    p.A = (const uint8_t *)A; p.lda = lda;
+    p.sA = sA; p.sa_m = sa_stride_m; p.sa_kb = sa_stride_kb;
+    p.B = (const uint8_t *)B; p.ldb = ldb; p.b_stride_g = b_stride_g;
+    p.sB = sB; p.sb_nb = sb_stride_nb; p.sb_kb = sb_stride_kb; p.sb_g = sb_stride_g;
+    p.D = (uint16_t *)D; p.ldd = ldd;
+    p.ids = expert_ids;
+    p.M = (int)M_total; p.N = (int)N; p.K = (int)K; p.G = (int)G;
+    return launch_tiles<dgk::kContiguous, 128, 128>(p, 1, dev.cus, (hipStream_t)stream);
+}
+
+int dg_fp8_grouped_gemm_masked(const void *A, int64_t lda, int64_t a_stride_g, const float *sA, int64_t sa_stride_g,
+                               int64_t sa_stride_m, int64_t sa_stride_kb, const void *B, int64_t ldb,
+                               int64_t b_stride_g, const float *sB, int64_t sb_stride_g, int64_t sb_stride_nb,
+                               int64_t sb_stride_kb, const int32_t *masked_m, void *D, int64_t ldd,
+                               int64_t d_stride_g, int64_t G, int64_t M_max, int64_t N, int64_t K, void *stream)
+{
+    int st = check_common_shape(M_max, N, K);
+    if (st != DG_OK)
+        return st;
+    if (G < 0)
+        return DG_ERR_BAD_SHAPE;
+    if (G > kInt32Max)
+        return DG_ERR_UNSUPPORTED;
+    if (G == 0 || M_max == 0 || N == 0)
+        return DG_OK;
+    if (!A || !sA || !B || !sB || !masked_m || !D)
+        return DG_ERR_NULL_POINTER;
+    if (lda < K || ldb < K || ldd < N || sa_stride_m < 0 || sa_stride_kb < 0 || sa_stride_g < 0 ||
+        sb_stride_nb < 0 || sb_stride_kb < 0 || sb_stride_g < 0 ||
+        (G > 1 && (a_stride_g < (M_max - 1) * lda + K || b_stride_g < (N - 1) * ldb + K ||
+                   d_stride_g < (M_max - 1) * ldd + N)))
+        return DG_ERR_BAD_STRIDE;
+    if (!aligned(A, 16) || !aligned(B, 16) || !aligned(D, 16) || lda % 16 || ldb % 16 || a_stride_g % 16 ||
+        b_stride_g % 16 || ldd % 8 || d_stride_g % 8 || !aligned(sA, 4) || !aligned(sB, 4) ||
+        !aligned(masked_m, 4))
+        return DG_ERR_MISALIGNED;
+    const int64_t nkb = K / 128;
+    const Extent ed = extent(D, 2, (G - 1) * d_stride_g + (M_max - 1) * ldd + N - 1);
+    if (overlaps(ed, extent(A, 1, (G - 1) * a_stride_g + (M_max - 1) * lda + K - 1)) ||
+        overlaps(ed, extent(B, 1, (G - 1) * b_stride_g + (N - 1) * ldb + K - 1)) ||
+        overlaps(ed, extent(sA, 4, (G - 1) * sa_stride_g + last_scale_index(M_max, nkb, sa_stride_m, sa_stride_kb))) ||
+        overlaps(ed, extent(sB, 4, (G - 1) * sb_stride_g + last_scale_index(N / 128, nkb, sb_stride_nb, sb_stride_kb))) ||
+        overlaps(ed, extent(masked_m, 4, G - 1)))
+        return DG_ERR_ALIASING;
+    DeviceInfo dev;
+    if ((st = current_device(dev)) != DG_OK)
+        return st;
+
+    dgk::Params p = {};
+    p.A = (const uint8_t *)A; p.lda = lda; p.a_stride_g = a_stride_g;
+    p.sA = sA; p.sa_m = sa_stride_m; p.sa_kb = sa_stride_kb; p.sa_g = sa_stride_g;
+    p.B = (const uint8_t *)B; p.ldb = ldb; p.b_stride_g = b_stride_g;
+    p.sB = sB; p.sb_nb = sb_stride_nb; p.sb_kb = sb_stride_kb; p.sb_g = sb_stride_g;
+    p.D = (uint16_t *)D; p.ldd = ldd; p.d_stride_g = d_stride_g;
+    p.masked_m = masked_m;
+    p.M = (int)M_max; p.N = (int)N; p.K = (int)K; p.G = (int)G;
+    return launch_tiles<dgk::kMasked, 128, 128>(p, (int)G, dev.cus, (hipStream_t)stream);
+}
+
+}  // extern "C"

@@ -1,0 +1,137 @@
+"""Python binding of the C ABI (include/dg_fp8.h), same names, torch tensors in.
+
+Argument marshalling only: every step of the GEMM runs in the HIP library.
+Operands are CUDA (HIP) tensors: e4m3 codes as ``torch.uint8`` or
+``torch.float8_e4m3fn``, scales ``torch.float32`` (any strides, read through
+the logical index), routing arrays ``torch.int32``, output ``torch.bfloat16``.
+The call is enqueued on torch's current stream unless ``stream`` is given.
+"""
+from __future__ import annotations
+
+import torch
+
+from . import _lib
+
+BLOCK = 128
+
+
+class DGError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        lib = _lib.load()
+        msg = lib.dg_status_string(status).decode()
+        if status == 6:  # DG_ERR_HIP
+            msg += " (hipError %d)" % lib.dg_last_hip_error()
+        super().__init__("%s: status %d: %s" % (where, status, msg))
+        self.status = status
+
+
+def _dev(t: torch.Tensor, name: str) -> int:
+    if not t.is_cuda:
+        raise ValueError("%s must be a device tensor" % name)
+    return t.data_ptr()
+
+
+def _codes(t: torch.Tensor, name: str, ndim: int) -> torch.Tensor:
+    if t.dtype not in (torch.uint8, torch.float8_e4m3fn):
+        raise TypeError("%s must hold e4m3 codes (uint8 or float8_e4m3fn)" % name)
+    if t.dim() != ndim or t.stride(-1) != 1:
+        raise ValueError("%s must be %d-D with a contiguous last (K) dimension" % (name, ndim))
+    return t
+
+
+def _scales(t: torch.Tensor, name: str, ndim: int) -> torch.Tensor:
+    if t.dtype != torch.float32 or t.dim() != ndim:
+        raise TypeError("%s must be a %d-D float32 tensor" % (name, ndim))
+    return t
+
+
+def _stream(stream) -> int:
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, torch.cuda.Stream):
+        return stream.cuda_stream
+    return int(stream)
+
+
+def _check(status: int, where: str):
+    if status != 0:
+        raise DGError(status, where)
+
+
+def dg_fp8_gemm_nt(a, sa, b, sb, d=None, stream=None):
+    """D[M,N] (bf16) from A[M,K], sA[M,K/128], B[N,K], sB[N/128,K/128]."""
+    _codes(a, "a", 2), _codes(b, "b", 2), _scales(sa, "sa", 2), _scales(sb, "sb", 2)
+    M, K = a.shape
+    N = b.shape[0]
+    if d is None:
+        d = torch.empty((M, N), dtype=torch.bfloat16, device=a.device)
+    if d.dtype != torch.bfloat16 or d.dim() != 2 or d.stride(-1) != 1:
+        raise TypeError("d must be a 2-D bfloat16 tensor with contiguous rows")
+    if b.shape[1] != K or tuple(d.shape) != (M, N):
+        raise ValueError("shape mismatch")
+    if tuple(sa.shape) != (M, K // BLOCK) or tuple(sb.shape) != (N // BLOCK, K // BLOCK):
+        raise ValueError("scale shape mismatch")
+    lib = _lib.load()
+    st = lib.dg_fp8_gemm_nt(_dev(a, "a"), a.stride(0), _dev(sa, "sa"), sa.stride(0), sa.stride(1),
+                            _dev(b, "b"), b.stride(0), _dev(sb, "sb"), sb.stride(0), sb.stride(1),
+                            _dev(d, "d"), d.stride(0), M, N, K, _stream(stream))
+    _check(st, "dg_fp8_gemm_nt")
+    return d
+
+
+def dg_fp8_grouped_gemm_contiguous(a, sa, b, sb, expert_ids, d=None, stream=None):
+    """Contiguous MoE layout: A[M_total,K], sA[M_total,K/128], B[G,N,K],
+    sB[G,N/128,K/128], expert_ids[M_total] int32 -> D[M_total,N]; rows whose
+    id is not in [0, G) are not written."""
+    _codes(a, "a", 2), _codes(b, "b", 3), _scales(sa, "sa", 2), _scales(sb, "sb", 3)
+    if expert_ids.dtype != torch.int32 or expert_ids.dim() != 1 or expert_ids.stride(0) != 1:
+        raise TypeError("expert_ids must be a contiguous 1-D int32 tensor")
+    M_total, K = a.shape
+    G, N, _ = b.shape
+    if d is None:
+        d = torch.empty((M_total, N), dtype=torch.bfloat16, device=a.device)
+    if d.dtype != torch.bfloat16 or d.dim() != 2 or d.stride(-1) != 1:
+        raise TypeError("d must be a 2-D bfloat16 tensor with contiguous rows")
+    if b.shape[2] != K or tuple(d.shape) != (M_total, N) or expert_ids.shape[0] != M_total:
+        raise ValueError("shape mismatch")
+    if tuple(sa.shape) != (M_total, K // BLOCK) or tuple(sb.shape) != (G, N // BLOCK, K // BLOCK):
+        raise ValueError("scale shape mismatch")
+    lib = _lib.load()
+    st = lib.dg_fp8_grouped_gemm_contiguous(
+        _dev(a, "a"), a.stride(0), _dev(sa, "sa"), sa.stride(0), sa.stride(1),
+        _dev(b, "b"), b.stride(1), b.stride(0),
+        _dev(sb, "sb"), sb.stride(0), sb.stride(1), sb.stride(2),
+        _dev(expert_ids, "expert_ids"), _dev(d, "d"), d.stride(0),
+        M_total, N, K, G, _stream(stream))
+    _check(st, "dg_fp8_grouped_gemm_contiguous")
+    return d
+
+
+def dg_fp8_grouped_gemm_masked(a, sa, b, sb, masked_m, d=None, stream=None):
+    """Masked MoE layout: A[G,M_max,K], sA[G,M_max,K/128], B[G,N,K],
+    sB[G,N/128,K/128], masked_m[G] int32 -> D[G,M_max,N]; group g writes rows
+    m < clamp(masked_m[g], 0, M_max) only."""
+    _codes(a, "a", 3), _codes(b, "b", 3), _scales(sa, "sa", 3), _scales(sb, "sb", 3)
+    if masked_m.dtype != torch.int32 or masked_m.dim() != 1 or masked_m.stride(0) != 1:
+        raise TypeError("masked_m must be a contiguous 1-D int32 tensor")
+    G, M_max, K = a.shape
+    N = b.shape[1]
+    if d is None:
+        d = torch.empty((G, M_max, N), dtype=torch.bfloat16, device=a.device)
+    if d.dtype != torch.bfloat16 or d.dim() != 3 or d.stride(-1) != 1:
+        raise TypeError("d must be a 3-D bfloat16 tensor with contiguous rows")
+    if (b.shape[0] != G or b.shape[2] != K or tuple(d.shape) != (G, M_max, N)
+            or masked_m.shape[0] != G):
+        raise ValueError("shape mismatch")
+    if tuple(sa.shape) != (G, M_max, K // BLOCK) or tuple(sb.shape) != (G, N // BLOCK, K // BLOCK):
+        raise ValueError("scale shape mismatch")
+    lib = _lib.load()
+    st = lib.dg_fp8_grouped_gemm_masked(
+        _dev(a, "a"), a.stride(1), a.stride(0),
+        _dev(sa, "sa"), sa.stride(0), sa.stride(1), sa.stride(2),
+        _dev(b, "b"), b.stride(1), b.stride(0),
+        _dev(sb, "sb"), sb.stride(0), sb.stride(1), sb.stride(2),
+        _dev(masked_m, "masked_m"), _dev(d, "d"), d.stride(1), d.stride(0),
+        G, M_max, N, K, _stream(stream))
+    _check(st, "dg_fp8_grouped_gemm_masked")
+    return d

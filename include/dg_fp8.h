@@ -1,0 +1,146 @@
+/*
+ * dg_fp8.h -- C ABI of the MI355X (gfx950) fine-grained block-scaled FP8 GEMM.
+ *
+ * Operation (all three entry points):
+ *
+ *   D[m, n] = bf16_rne( sum_kb  sA[m, kb] * sB[n/128, kb]
+ *                               * sum_{k in [128 kb, 128 kb + 128)} A[m, k] * B[n, k] )
+ *
+ *   - A and B hold OCP e4m3 codes (1 sign, 4 exponent bits with bias 7,
+ *     3 mantissa bits, largest finite 448, no infinity): rkmt.cn DeepGEMM
+ *     walkthrough §2.1 and §5.2; lpnh.cn DeepGEMM article §2.1.
+ *   - LHS scales cover 1x128 tiles (one fp32 per row and 128-wide K block),
+ *     RHS scales cover 128x128 tiles: hotdry.top fine-grained scaling article,
+ *     "fine-grained scaling core design".
+ *   - Each 128-wide K block's partial product is multiplied by sA*sB before
+ *     it is added to an fp32 accumulator, because the scale product changes
+ *     from block to block: lpnh.cn §2.3; hotdry.top "two-level accumulation".
+ *   - The output is bf16 (round to nearest even). D is overwritten; there is
+ *     no C/bias term and no accumulation into D.
+ *
+ * "NT": A is [M, K] and B is [N, K], both with K contiguous, D = A . B^T.
+ *
+ * Conventions shared by every entry point
+ *   - All pointers are DEVICE pointers owned by the caller. The library never
+ *     allocates, frees, keeps a pointer past return, or synchronises.
+ *   - `stream` is a hipStream_t (NULL = the legacy default stream). The call
+ *     validates its arguments on the host, enqueues one kernel and returns.
+ *   - Strides are in elements. e4m3 is one byte, so A/B strides are also byte
+ *     strides; D strides count bf16 elements. Scale tables are addressed
+ *     logically through explicit strides: sA[m, kb] = sA[m*sa_stride_m +
+ *     kb*sa_stride_kb], sB[nb, kb] = sB[nb*sb_stride_nb + kb*sb_stride_kb].
+ *     Row-major and M-major scale layouts are both legal; a zero stride
+ *     broadcasts (e.g. per-tensor scales).
+ *   - Alignment: A, B and D base addresses 16-byte aligned; lda, ldb and the
+ *     grouped byte strides multiples of 16; ldd (and d_stride_g) multiples of
+ *     8 elements; scale pointers 4-byte aligned.
+ *   - Shapes: K > 0 and K % 128 == 0; N % 128 == 0; M arbitrary (>= 0).
+ *   - D must not overlap A, B, sA, sB or the routing arrays.
+ *   - Results are deterministic: no atomics, a fixed reduction order.
+ *   - Thread-safe; the only global state is a per-device property cache.
+ *
+ * Errors: every error is detected on the host before anything is enqueued,
+ * and D is left untouched. DG_ERR_HIP reports a failed launch; the HIP error
+ * code is kept per thread (dg_last_hip_error). An empty problem (M = 0,
+ * N = 0, M_total = 0 or G = 0) returns DG_OK without launching.
+ */
+#ifndef DG_FP8_H
+#define DG_FP8_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define DG_ABI_VERSION 1
+
+enum {
+    DG_OK = 0,
+    DG_ERR_NULL_POINTER = 1, /* a required pointer is NULL for a non-empty problem */
+    DG_ERR_BAD_SHAPE = 2,    /* negative dim, K <= 0, K % 128, N % 128, M_total % 128 */
+    DG_ERR_MISALIGNED = 3,   /* base pointer or stride violates the alignment rules */
+    DG_ERR_BAD_STRIDE = 4,   /* lda < K, ldb < K, ldd < N, negative or too small group stride */
+    DG_ERR_UNSUPPORTED = 5,  /* current device is not gfx950, or a size exceeds int32 */
+    DG_ERR_HIP = 6,          /* the HIP runtime failed (query or launch) */
+    DG_ERR_ALIASING = 7      /* D overlaps an input */
+};
+
+/* Version of this ABI (DG_ABI_VERSION). */
+int dg_abi_version(void);
+
+/* Static, human-readable text for a status code (never NULL). */
+const char *dg_status_string(int status);
+
+/* hipError_t of the last DG_ERR_HIP returned on the calling thread (0 if none). */
+int dg_last_hip_error(void);
+
+/*
+ * Dense NT GEMM.
+ *   A  [M, K] e4m3, row stride lda          sA fp32, logical [M, K/128]
+ *   B  [N, K] e4m3, row stride ldb          sB fp32, logical [N/128, K/128]
+ *   D  [M, N] bf16, row stride ldd (written)
+ * Operation as in the header comment (lpnh.cn §2.3; hotdry.top, fine-grained
+ * scaling core design).
+ */
+int dg_fp8_gemm_nt(const void *A, int64_t lda,
+                   const float *sA, int64_t sa_stride_m, int64_t sa_stride_kb,
+                   const void *B, int64_t ldb,
+                   const float *sB, int64_t sb_stride_nb, int64_t sb_stride_kb,
+                   void *D, int64_t ldd,
+                   int64_t M, int64_t N, int64_t K, void *stream);
+
+/*
+ * Grouped GEMM, contiguous layout (MoE): the rows of all experts are stacked
+ * in one LHS, each expert's rows contiguous and padded to a multiple of 128,
+ * and expert_ids[r] names the expert of row r (one launch for all experts:
+ * rkmt.cn walkthrough §1.2 and §5.3; hotdry.top, grouped GEMM parameters).
+ *   A  [M_total, K] e4m3, row stride lda    sA logical [M_total, K/128]
+ *   B  [G, N, K] e4m3: expert e at B + e*b_stride_g, row stride ldb
+ *   sB logical [G, N/128, K/128]: sB[e, nb, kb] = sB[e*sb_stride_g + nb*sb_stride_nb + kb*sb_stride_kb]
+ *   expert_ids [M_total] int32, device memory
+ *   D  [M_total, N] bf16, row stride ldd
+ * Row r is computed against expert expert_ids[r] when 0 <= id < G. Rows whose
+ * id is -1 (padding) or outside [0, G) are NOT written.
+ * Layout contract: M_total % 128 == 0 and within every aligned 128-row block
+ * all ids in [0, G) are equal (segments padded to 128). A block's expert is
+ * the largest id in the block; a row whose id differs from it is not written.
+ */
+int dg_fp8_grouped_gemm_contiguous(const void *A, int64_t lda,
+                                   const float *sA, int64_t sa_stride_m, int64_t sa_stride_kb,
+                                   const void *B, int64_t ldb, int64_t b_stride_g,
+                                   const float *sB, int64_t sb_stride_g, int64_t sb_stride_nb,
+                                   int64_t sb_stride_kb,
+                                   const int32_t *expert_ids,
+                                   void *D, int64_t ldd,
+                                   int64_t M_total, int64_t N, int64_t K, int64_t G, void *stream);
+
+/*
+ * Grouped GEMM, masked layout (MoE decode): every expert owns a fixed block
+ * of M_max rows and masked_m[g] (device memory, read by the kernel, so the
+ * call needs no host synchronisation and the counts may change between
+ * replays of a captured launch: bhfrc.com DeepGEMM article §4.3) says how
+ * many of them are valid.
+ *   A  [G, M_max, K] e4m3: A_g = A + g*a_stride_g, row stride lda
+ *   sA logical [G, M_max, K/128]: sA[g*sa_stride_g + m*sa_stride_m + kb*sa_stride_kb]
+ *   B  [G, N, K], sB [G, N/128, K/128] as in the contiguous call
+ *   masked_m [G] int32, device memory
+ *   D  [G, M_max, N] bf16: D_g = D + g*d_stride_g, row stride ldd
+ * Group g writes rows m < clamp(masked_m[g], 0, M_max); all other rows of D
+ * are NOT written.
+ */
+int dg_fp8_grouped_gemm_masked(const void *A, int64_t lda, int64_t a_stride_g,
+                               const float *sA, int64_t sa_stride_g, int64_t sa_stride_m,
+                               int64_t sa_stride_kb,
+                               const void *B, int64_t ldb, int64_t b_stride_g,
+                               const float *sB, int64_t sb_stride_g, int64_t sb_stride_nb,
+                               int64_t sb_stride_kb,
+                               const int32_t *masked_m,
+                               void *D, int64_t ldd, int64_t d_stride_g,
+                               int64_t G, int64_t M_max, int64_t N, int64_t K, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DG_FP8_H */

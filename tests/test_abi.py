@@ -1,0 +1,138 @@
+"""The C-ABI library loads, exports every symbol its header declares, and
+rejects bad arguments on the host (these calls return before any device
+access, so they run without a GPU)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from fp8_block_scaled_sa_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "dg_fp8.h")
+
+DG_OK, DG_ERR_NULL_POINTER, DG_ERR_BAD_SHAPE, DG_ERR_MISALIGNED = 0, 1, 2, 3
+DG_ERR_BAD_STRIDE, DG_ERR_UNSUPPORTED, DG_ERR_HIP, DG_ERR_ALIASING = 4, 5, 6, 7
+
+
+def declared_symbols():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:int|const char \*)\s*(dg_\w+)\s*\(", text, re.M)))
+
+
+def test_header_declares_the_entry_points():
+    syms = declared_symbols()
+    for name in ("dg_fp8_gemm_nt", "dg_fp8_grouped_gemm_contiguous", "dg_fp8_grouped_gemm_masked",
+                 "dg_abi_version", "dg_status_string", "dg_last_hip_error"):
+        assert name in syms
+
+
+def test_library_exports_every_declared_symbol():
+    lib = ctypes.CDLL(_lib.path())
+    for name in declared_symbols():
+        assert hasattr(lib, name), name
+    assert set(declared_symbols()) == set(_lib.SIGNATURES)
+
+
+def test_version_and_status_strings():
+    lib = _lib.load()
+    assert lib.dg_abi_version() == 1
+    for s in range(8):
+        assert lib.dg_status_string(s)
+    assert lib.dg_status_string(99) == b"unknown status"
+    assert lib.dg_last_hip_error() == 0
+
+
+# Fake, never-dereferenced, 256-byte aligned addresses that do not overlap.
+A, SA, B, SB, D, IDS = (0x10000000 * (i + 1) for i in range(6))
+
+
+def nt(**kw):
+    args = dict(A=A, lda=512, sA=SA, sa_m=1, sa_kb=64, B=B, ldb=512, sB=SB, sb_nb=4, sb_kb=1,
+                D=D, ldd=256, M=64, N=256, K=512, stream=None)
+    args.update(kw)
+    return _lib.load().dg_fp8_gemm_nt(*args.values())
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(K=500, lda=512, ldb=512), DG_ERR_BAD_SHAPE),
+    (dict(K=0), DG_ERR_BAD_SHAPE),
+    (dict(N=200), DG_ERR_BAD_SHAPE),
+    (dict(M=-1), DG_ERR_BAD_SHAPE),
+    (dict(A=None), DG_ERR_NULL_POINTER),
+    (dict(sB=None), DG_ERR_NULL_POINTER),
+    (dict(D=None), DG_ERR_NULL_POINTER),
+    (dict(lda=256), DG_ERR_BAD_STRIDE),
+    (dict(ldb=384), DG_ERR_BAD_STRIDE),
+    (dict(ldd=128), DG_ERR_BAD_STRIDE),
+    (dict(sa_m=-1), DG_ERR_BAD_STRIDE),
+    (dict(A=A + 8), DG_ERR_MISALIGNED),
+    (dict(D=D + 2), DG_ERR_MISALIGNED),
+    (dict(lda=520), DG_ERR_MISALIGNED),
+    (dict(ldd=260), DG_ERR_MISALIGNED),
+    (dict(sA=SA + 2), DG_ERR_MISALIGNED),
+    (dict(D=A + 1024), DG_ERR_ALIASING),
+    (dict(D=SB), DG_ERR_ALIASING),
+    (dict(M=2 ** 31), DG_ERR_UNSUPPORTED),
+])
+def test_dense_validation(kw, status):
+    assert nt(**kw) == status
+
+
+def test_empty_problems_return_ok_without_device():
+    assert nt(M=0) == DG_OK
+    assert nt(N=0) == DG_OK
+    assert nt(M=0, A=None, B=None, D=None) == DG_OK
+
+
+def contig(**kw):
+    args = dict(A=A, lda=512, sA=SA, sa_m=1, sa_kb=256, B=B, ldb=512, b_stride_g=256 * 512,
+                sB=SB, sb_g=8, sb_nb=4, sb_kb=1, ids=IDS, D=D, ldd=256,
+                M_total=256, N=256, K=512, G=4, stream=None)
+    args.update(kw)
+    return _lib.load().dg_fp8_grouped_gemm_contiguous(*args.values())
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(M_total=200), DG_ERR_BAD_SHAPE),
+    (dict(G=-1), DG_ERR_BAD_SHAPE),
+    (dict(ids=None), DG_ERR_NULL_POINTER),
+    (dict(b_stride_g=1024), DG_ERR_BAD_STRIDE),
+    (dict(b_stride_g=256 * 512 + 8), DG_ERR_MISALIGNED),
+    (dict(ids=IDS + 2), DG_ERR_MISALIGNED),
+    (dict(D=IDS), DG_ERR_ALIASING),
+])
+def test_contiguous_validation(kw, status):
+    assert contig(**kw) == status
+
+
+def test_contiguous_empty():
+    assert contig(M_total=0) == DG_OK
+    assert contig(G=0) == DG_OK
+
+
+def masked(**kw):
+    args = dict(A=A, lda=512, a_stride_g=64 * 512, sA=SA, sa_g=256, sa_m=1, sa_kb=64,
+                B=B, ldb=512, b_stride_g=256 * 512, sB=SB, sb_g=8, sb_nb=4, sb_kb=1,
+                masked_m=IDS, D=D, ldd=256, d_stride_g=64 * 256,
+                G=4, M_max=64, N=256, K=512, stream=None)
+    args.update(kw)
+    return _lib.load().dg_fp8_grouped_gemm_masked(*args.values())
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(K=100), DG_ERR_BAD_SHAPE),
+    (dict(masked_m=None), DG_ERR_NULL_POINTER),
+    (dict(a_stride_g=512), DG_ERR_BAD_STRIDE),
+    (dict(d_stride_g=256), DG_ERR_BAD_STRIDE),
+    (dict(d_stride_g=64 * 256 + 4), DG_ERR_MISALIGNED),
+    (dict(D=B + 4096), DG_ERR_ALIASING),
+])
+def test_masked_validation(kw, status):
+    assert masked(**kw) == status
+
+
+def test_masked_empty():
+    assert masked(G=0) == DG_OK
+    assert masked(M_max=0) == DG_OK
