@@ -4,6 +4,7 @@
 #include <hip/hip_runtime.h>
 
 #include <mutex>
+#include <stdlib.h>
 #include <stdint.h>
 #include <string.h>
 
@@ -88,44 +89,60 @@ int64_t last_scale_index(int64_t rows, int64_t nkb, int64_t s_row, int64_t s_kb)
     return (rows - 1) * s_row + (nkb - 1) * s_kb;
 }
 
-template <typename Kern>
-int launch(Kern kernel, int grid, hipStream_t stream, const dgk::Params &p)
+// Tile configurations (BM, BN, waves M x N, LDS stages, tile-order group).
+// 256x128 tiles split 4096- and 8192-row problems into whole waves of the
+// 256 CUs; each holds 3 stages of 49 KB in LDS, one workgroup per CU, with
+// 8 waves (2 per SIMD) so one wave's promotion FMAs overlap another's MFMAs.
+using CfgDense = dgk::TileCfg<256, 128, 4, 2, 3, 4>;
+using CfgDense4 = dgk::TileCfg<256, 128, 2, 2, 3, 4>;
+using CfgWide = dgk::TileCfg<128, 256, 2, 2, 3, 8>;
+using CfgNarrow = dgk::TileCfg<128, 128, 2, 2, 4, 8>;
+
+// Optional override of the tile configuration, read once: DG_TILE=<index>.
+int tile_override()
 {
-    hipLaunchKernelGGL(kernel, dim3(grid), dim3(dgk::kThreads), 0, stream, p);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess)
-        return fail_hip(e);
-    return DG_OK;
+    static int v = [] {
+        const char *e = getenv("DG_TILE");
+        return e ? atoi(e) : -1;
+    }();
+    return v;
 }
 
-// Workgroups resident per CU for the tile kernels (LDS and registers allow 2).
-constexpr int kTileOccupancy = 2;
-
-template <int L, int BM, int BN>
+template <int L, class C>
 int launch_tiles(dgk::Params &p, int groups, int cus, hipStream_t stream)
 {
-    p.tiles_m = (int)((p.M + BM - 1) / BM);
-    p.tiles_n = p.N / BN;
+    p.tiles_m = (int)((p.M + C::kBM - 1) / C::kBM);
+    p.tiles_n = p.N / C::kBN;
     const int64_t tiles = (int64_t)p.tiles_m * p.tiles_n * groups;
     if (tiles > kInt32Max)
         return DG_ERR_UNSUPPORTED;
     p.num_tiles = (int)tiles;
     if (p.num_tiles == 0)
         return DG_OK;
-    int grid = cus * kTileOccupancy;
-    if (p.num_tiles < grid)
-        grid = p.num_tiles;
-    return launch(dgk::tile_kernel<L, BM, BN>, grid, stream, p);
+    const int grid = p.num_tiles < cus ? p.num_tiles : cus;  // persistent: one workgroup per CU
+    hipLaunchKernelGGL((dgk::tile_kernel<L, C>), dim3(grid), dim3(C::kThreads), 0, stream, p);
+    hipError_t e = hipGetLastError();
+    return e == hipSuccess ? DG_OK : fail_hip(e);
+}
+
+// Per-lane DMA offsets are 32-bit: a tile's rows of A, B and sA must span < 2^32 bytes.
+bool offsets_fit(int64_t lda, int64_t ldb, int64_t sa_stride_m)
+{
+    return lda <= (1 << 22) && ldb <= (1 << 22) && sa_stride_m <= (1 << 20);
 }
 
 int launch_decode(dgk::Params &p, hipStream_t stream)
 {
     const int grid = p.N / 16;
+    hipError_t e;
     if (p.M <= 16)
-        return launch(dgk::decode_kernel<1>, grid, stream, p);
-    if (p.M <= 32)
-        return launch(dgk::decode_kernel<2>, grid, stream, p);
-    return launch(dgk::decode_kernel<4>, grid, stream, p);
+        hipLaunchKernelGGL(dgk::decode_kernel<1>, dim3(grid), dim3(dgk::kDecodeThreads), 0, stream, p);
+    else if (p.M <= 32)
+        hipLaunchKernelGGL(dgk::decode_kernel<2>, dim3(grid), dim3(dgk::kDecodeThreads), 0, stream, p);
+    else
+        hipLaunchKernelGGL(dgk::decode_kernel<4>, dim3(grid), dim3(dgk::kDecodeThreads), 0, stream, p);
+    e = hipGetLastError();
+    return e == hipSuccess ? DG_OK : fail_hip(e);
 }
 
 }  // namespace
@@ -186,9 +203,15 @@ int dg_fp8_gemm_nt(const void *A, int64_t lda, const float *sA, int64_t sa_strid
     p.D = (uint16_t *)D; p.ldd = ldd;
     p.M = (int)M; p.N = (int)N; p.K = (int)K; p.G = 1;
     hipStream_t s = (hipStream_t)stream;
-    if (M <= 64)
+    if (M <= 64 && tile_override() < 0)
         return launch_decode(p, s);
-    return launch_tiles<dgk::kDense, 128, 128>(p, 1, dev.cus, s);
+    if (!offsets_fit(lda, ldb, sa_stride_m))
+        return DG_ERR_UNSUPPORTED;
+    switch (tile_override()) {
+    case 1: return launch_tiles<dgk::kDense, CfgDense4>(p, 1, dev.cus, s);
+    case 2: return launch_tiles<dgk::kDense, CfgNarrow>(p, 1, dev.cus, s);
+    default: return launch_tiles<dgk::kDense, CfgDense>(p, 1, dev.cus, s);
+    }
 }
 
 int dg_fp8_grouped_gemm_contiguous(const void *A, int64_t lda, const float *sA, int64_t sa_stride_m,
@@ -234,7 +257,11 @@ int dg_fp8_grouped_gemm_contiguous(const void *A, int64_t lda, const float *sA, 
     p.D = (uint16_t *)D; p.ldd = ldd;
     p.ids = expert_ids;
     p.M = (int)M_total; p.N = (int)N; p.K = (int)K; p.G = (int)G;
-    return launch_tiles<dgk::kContiguous, 128, 128>(p, 1, dev.cus, (hipStream_t)stream);
+    if (!offsets_fit(lda, ldb, sa_stride_m))
+        return DG_ERR_UNSUPPORTED;
+    if (N % 256 == 0 && tile_override() != 2)
+        return launch_tiles<dgk::kContiguous, CfgWide>(p, 1, dev.cus, (hipStream_t)stream);
+    return launch_tiles<dgk::kContiguous, CfgNarrow>(p, 1, dev.cus, (hipStream_t)stream);
 }
 
 int dg_fp8_grouped_gemm_masked(const void *A, int64_t lda, int64_t a_stride_g, const float *sA, int64_t sa_stride_g,
@@ -283,7 +310,13 @@ int dg_fp8_grouped_gemm_masked(const void *A, int64_t lda, int64_t a_stride_g, c
     p.D = (uint16_t *)D; p.ldd = ldd; p.d_stride_g = d_stride_g;
     p.masked_m = masked_m;
     p.M = (int)M_max; p.N = (int)N; p.K = (int)K; p.G = (int)G;
-    return launch_tiles<dgk::kMasked, 128, 128>(p, (int)G, dev.cus, (hipStream_t)stream);
+    if (!offsets_fit(lda, ldb, sa_stride_m))
+        return DG_ERR_UNSUPPORTED;
+    switch (tile_override()) {
+    case 1: return launch_tiles<dgk::kMasked, CfgDense4>(p, (int)G, dev.cus, (hipStream_t)stream);
+    case 2: return launch_tiles<dgk::kMasked, CfgNarrow>(p, (int)G, dev.cus, (hipStream_t)stream);
+    default: return launch_tiles<dgk::kMasked, CfgDense>(p, (int)G, dev.cus, (hipStream_t)stream);
+    }
 }
 
 }  // extern "C"

@@ -16,10 +16,18 @@
 // up with ONE row m of D (lane % 16) and four consecutive columns n
 // (4 * (lane / 16) + r). One scale product per lane per K block, and an
 // 8-byte store per 16x16 sub-tile.
+//
+// K order inside a block: lane group lg = lane / 16 hands the MFMA bytes
+// [16 lg, 16 lg + 16) and [64 + 16 lg, 64 + 16 lg + 16) of the block, for A
+// and B alike. The MFMA sums over all 128 positions, so any permutation of K
+// that is the same for both operands gives the same dot product; this one
+// makes each 16-lane group of a load instruction read 64 contiguous bytes.
 #pragma once
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
+
+#include <type_traits>
 
 namespace dgk {
 
@@ -83,37 +91,61 @@ __device__ __forceinline__ v8i join(const uint4 &lo, const uint4 &hi)
 }
 
 // ---------------------------------------------------------------------------
-// LDS tile layout: a tile of R rows x 128 bytes (one K block), row-major, with
-// the eight 16-byte chunks of each row XOR-permuted by swz(row). A 128-bit
-// LDS read by 16 lanes of 16 consecutive rows at one logical chunk then hits
-// 16 distinct 16-byte bank groups (and any 8 consecutive rows hit 8), and a
-// 128-bit write of one row's 8 chunks by 8 lanes is conflict-free as well.
+// Low-level pieces of the LDS pipeline.
+//
+// Operand tiles are copied HBM -> LDS with gfx950's LDS-DMA loads
+// (global_load_lds_dwordx4 / _dword): each lane names a global address and
+// the data lands at M0 + 16 * lane (4 * lane for the dword form), bypassing
+// VGPRs. They are issued through inline asm, together with the waits and the
+// barrier, so that the compiler neither serialises them (it would wait for
+// every outstanding DMA before each LDS read) nor fences the barrier (HIP's
+// __syncthreads waits for all outstanding loads). The pipeline tracks
+// completion itself with vmcnt: vector loads of a wave complete in issue
+// order, so "at most n outstanding" means everything but the last n issued
+// has landed.
+
+__device__ __forceinline__ uint32_t lds_addr(const void *p)
+{
+    return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void *)p;
+}
+
+// 16 bytes per lane from base + voff into LDS at m0 + 16 * lane.
+__device__ __forceinline__ void dma_b128(const void *base, uint32_t voff, uint32_t m0)
+{
+    asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(base), "s"(m0)
+                 : "memory", "m0");
+}
+
+// 4 bytes per lane from base + voff into LDS at m0 + 4 * lane.
+__device__ __forceinline__ void dma_b32(const void *base, uint32_t voff, uint32_t m0)
+{
+    asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dword %0, %1" ::"v"(voff), "s"(base), "s"(m0)
+                 : "memory", "m0");
+}
+
+template <int N>
+__device__ __forceinline__ void wait_vmcnt()
+{
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+__device__ __forceinline__ void wg_barrier() { asm volatile("s_barrier" ::: "memory"); }
+
+// LDS tile layout: R rows x 128 bytes (one K block), row-major, with the
+// eight 16-byte chunks of each row XOR-permuted by swz(row). A 128-bit LDS
+// read of one logical chunk by 16 lanes of 16 consecutive rows hits 16
+// distinct 16-byte bank groups (any 8 consecutive rows hit 8).
 __device__ __forceinline__ int swz(int row) { return (row ^ (row >> 3)) & 7; }
 
 __device__ __forceinline__ int lds_off(int row, int chunk) { return row * 128 + ((chunk ^ swz(row)) << 4); }
 
-// 32 bytes of one row's K block for the MFMA operand of lane group lg.
+// The 32 operand bytes of lane group lg for one tile row: chunks lg and lg+4.
 __device__ __forceinline__ v8i lds_frag(const uint8_t *tile, int row, int lg)
 {
-    const uint4 lo = *reinterpret_cast<const uint4 *>(tile + lds_off(row, 2 * lg));
-    const uint4 hi = *reinterpret_cast<const uint4 *>(tile + lds_off(row, 2 * lg + 1));
+    const uint4 lo = *reinterpret_cast<const uint4 *>(tile + lds_off(row, lg));
+    const uint4 hi = *reinterpret_cast<const uint4 *>(tile + lds_off(row, lg + 4));
     return join(lo, hi);
-}
-
-constexpr int kThreads = 256;  // 4 waves of 64
-constexpr int kGroupM = 8;     // tile-order super-row height (L2 reuse)
-
-// Tile index -> (m tile, n tile): runs of kGroupM m-tiles are walked m-first,
-// so any window of consecutive tile indices is close to square in (m, n).
-__device__ __forceinline__ void tile_coords(int t, int tiles_m, int tiles_n, int &mt, int &nt)
-{
-    const int per_group = kGroupM * tiles_n;
-    const int group = t / per_group;
-    const int within = t - group * per_group;
-    const int first_m = group * kGroupM;
-    const int gm = min(kGroupM, tiles_m - first_m);
-    mt = first_m + within % gm;
-    nt = within / gm;
 }
 
 // Workgroups are dispatched round-robin over the 8 XCDs. Renumber them so each
@@ -126,47 +158,98 @@ __device__ __forceinline__ int xcd_local_id(int b, int grid)
     return (b & 7) * (grid >> 3) + (b >> 3);
 }
 
-template <int BM, int BN>
-struct TileSmem {
-    uint8_t a[2][BM * 128];
-    uint8_t b[2][BN * 128];
-    float sa[2][BM];
+// Tile index -> (m tile, n tile): runs of group_m m-tiles are walked m-first,
+// so any window of consecutive tile indices is close to square in (m, n).
+__device__ __forceinline__ void tile_coords(int t, int tiles_m, int tiles_n, int group_m, int &mt, int &nt)
+{
+    const int per_group = group_m * tiles_n;
+    const int group = t / per_group;
+    const int within = t - group * per_group;
+    const int first_m = group * group_m;
+    const int gm = min(group_m, tiles_m - first_m);
+    mt = first_m + within % gm;
+    nt = within / gm;
+}
+
+// ---------------------------------------------------------------------------
+// Persistent, multi-stage LDS-DMA pipelined tile kernel.
+//
+// Workgroup tile BM x BN (BN a multiple of 128 is not required, but a wave's
+// columns must lie in one 128-wide sB block), WAVES_M x WAVES_N waves, each
+// owning a (BM/WAVES_M) x (BN/WAVES_N) block of 16x16 sub-tiles. STAGES LDS
+// buffers, each holding one K block of the A tile, the B tile and sA.
+template <int BM, int BN, int WAVES_M, int WAVES_N, int STAGES, int GROUP_M>
+struct TileCfg {
+    static constexpr int kBM = BM, kBN = BN, kStages = STAGES, kGroupM = GROUP_M;
+    static constexpr int kWavesM = WAVES_M, kWavesN = WAVES_N;
+    static constexpr int kWaves = WAVES_M * WAVES_N;
+    static constexpr int kThreads = kWaves * 64;
+    static constexpr int kWM = BM / WAVES_M, kWN = BN / WAVES_N;
+    static constexpr int kMI = kWM / 16, kNJ = kWN / 16;
+    static constexpr int kSegA = BM / 8, kSegB = BN / 8;     // 1 KB LDS segments (8 rows)
+    static constexpr int kSegPerWave = (kSegA + kSegB) / kWaves;
+    static constexpr int kSaLoads = BM / 64;                  // dword DMA instructions for sA
+    static constexpr int kOffB = BM * 128, kOffSa = kOffB + BN * 128, kOffSb = kOffSa + BM * 4;
+    static constexpr int kStageBytes = kOffSb + 256;       // + 64 sB slots (one per 128 columns)
+    static constexpr int kNB = BN / 128;                    // sB blocks per tile
+    static constexpr int kSmemBytes = STAGES * kStageBytes;
+    static_assert(kWM % 16 == 0 && kWN % 16 == 0, "wave tile");
+    static_assert((kSegA + kSegB) % kWaves == 0, "segments split evenly over waves");
+    static_assert(BM % 64 == 0 && kSaLoads <= kWaves, "sA loads");
+    static_assert(kWN <= 128 && (128 % kWN) == 0, "a wave's columns share one sB block");
+    static_assert(BN % 128 == 0, "tile columns cover whole sB blocks");
+    static_assert(STAGES >= 2 && STAGES <= 4, "pipeline depth (the K loop is unrolled by at most 4)");
+    static_assert(kSmemBytes <= 160 * 1024, "LDS");
+    static_assert((kSegPerWave + 2) * (STAGES - 2) < 64, "vmcnt range");
 };
 
-// Persistent, LDS double-buffered tile kernel. Workgroup tile BM x BN, 2x2
-// waves, each wave a (BM/2) x (BN/2) block of 16x16 MFMA sub-tiles.
-template <int L, int BM, int BN>
-__global__ void __launch_bounds__(kThreads) tile_kernel(Params p)
+// Wait until this wave's DMA for the oldest pipeline stage has landed: at most
+// `later` stages of `per_stage` loads each may still be in flight.
+template <int SEGW, int LATER>
+__device__ __forceinline__ void wait_stage(int per_stage)
 {
-    constexpr int WM = BM / 2, WN = BN / 2;
-    constexpr int MI = WM / 16, NJ = WN / 16;
-    constexpr int LA = BM * 8 / kThreads;  // 16-byte chunks per thread per K block
-    constexpr int LB = BN * 8 / kThreads;
-    static_assert(BM % 32 == 0 && BN % 32 == 0, "tile");
-    static_assert((BM * 8) % kThreads == 0 && (BN * 8) % kThreads == 0, "tile loads");
-    static_assert(WN <= 128 && (128 % WN) == 0, "a wave's columns share one sB block");
-    static_assert(L != kContiguous || (128 % BM) == 0, "contiguous tiles stay inside one 128-row block");
+    if (per_stage == SEGW)
+        wait_vmcnt<SEGW * LATER>();
+    else if (per_stage == SEGW + 1)
+        wait_vmcnt<(SEGW + 1) * LATER>();
+    else
+        wait_vmcnt<(SEGW + 2) * LATER>();
+}
 
-    __shared__ __attribute__((aligned(16))) TileSmem<BM, BN> sm;
+template <int L, class C>
+__global__ void __launch_bounds__(C::kThreads, 1) tile_kernel(Params p)
+{
+    constexpr int BM = C::kBM, BN = C::kBN, S = C::kStages;
+    constexpr int MI = C::kMI, NJ = C::kNJ;
+    constexpr int SEGW = C::kSegPerWave;
+    static_assert(L != kContiguous || BM <= 128, "contiguous tiles stay inside one 128-row block");
+
+    __shared__ __attribute__((aligned(1024))) uint8_t smem[C::kSmemBytes];
 
     const int tid = threadIdx.x;
-    const int lane = tid & 63, wave = tid >> 6;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int l16 = lane & 15, lg = lane >> 4;
-    const int wm0 = (wave >> 1) * WM, wn0 = (wave & 1) * WN;
+    const int wm0 = (wave / C::kWavesN) * C::kWM;
+    const int wn0 = (wave % C::kWavesN) * C::kWN;
     const int nk = p.K >> 7;
     const int tiles_per_group = p.tiles_m * p.tiles_n;
+    const uint32_t smem_base = lds_addr(smem);
+    const bool loads_sa = wave < C::kSaLoads;
+    const bool loads_sb = wave == C::kWaves - 1;
+    const int per_stage = SEGW + (loads_sa ? 1 : 0) + (loads_sb ? 1 : 0);  // DMA ops per stage
 
     for (int t = xcd_local_id(blockIdx.x, gridDim.x); t < p.num_tiles; t += gridDim.x) {
         int g = 0, mt, nt;
         if (L == kMasked) {
             g = t / tiles_per_group;
-            tile_coords(t - g * tiles_per_group, p.tiles_m, p.tiles_n, mt, nt);
+            tile_coords(t - g * tiles_per_group, p.tiles_m, p.tiles_n, C::kGroupM, mt, nt);
         } else {
-            tile_coords(t, p.tiles_m, p.tiles_n, mt, nt);
+            tile_coords(t, p.tiles_m, p.tiles_n, C::kGroupM, mt, nt);
         }
         const int m0 = mt * BM, n0 = nt * BN;
 
-        int rows;        // rows of this tile that are loaded (others read as 0)
+        int rows;        // valid rows of this tile (the rest re-read the last valid row)
         int limit = 0;   // masked: valid rows of the group
         int expert = 0;  // group whose B/sB this tile uses
         if (L == kDense) {
@@ -186,50 +269,52 @@ __global__ void __launch_bounds__(kThreads) tile_kernel(Params p)
             int e = max(e0, e1);
             for (int o = 32; o > 0; o >>= 1)
                 e = max(e, __shfl_xor(e, o));
+            e = __builtin_amdgcn_readfirstlane(e);
             if (e < 0)
                 continue;
             expert = e;
-            rows = BM;
+            rows = min(BM, p.M - m0);
         }
 
         const uint8_t *Ab = p.A + (int64_t)g * p.a_stride_g + (int64_t)m0 * p.lda;
         const uint8_t *Bb = p.B + (int64_t)expert * p.b_stride_g + (int64_t)n0 * p.ldb;
         const float *sAb = p.sA + (int64_t)g * p.sa_g + (int64_t)m0 * p.sa_m;
-        const float *sBw = p.sB + (int64_t)expert * p.sb_g + (int64_t)((n0 + wn0) >> 7) * p.sb_nb;
+        const float *sBb = p.sB + (int64_t)expert * p.sb_g + (int64_t)(n0 >> 7) * p.sb_nb;
 
-        uint4 ra[LA], rb[LB];
-        float rsa = 0.f;
+        // Per-lane byte offsets of this wave's DMA segments (constant over K).
+        // Segment s covers tile rows 8s..8s+7 (A rows first, then B rows);
+        // lane i fills LDS bytes 16 i of it: row 8s + i/8, physical chunk
+        // i%8, i.e. logical chunk (i%8) ^ swz(row).
+        uint32_t voff[SEGW];
+#pragma unroll
+        for (int q = 0; q < SEGW; ++q) {
+            const int seg = q * C::kWaves + wave;
+            if (seg < C::kSegA) {
+                int row = seg * 8 + (lane >> 3);
+                const int ch = (lane & 7) ^ swz(row);
+                row = min(row, rows - 1);
+                voff[q] = (uint32_t)(row * p.lda + ch * 16);
+            } else {
+                const int row = (seg - C::kSegA) * 8 + (lane >> 3);
+                const int ch = (lane & 7) ^ swz(row);
+                voff[q] = (uint32_t)(row * p.ldb + ch * 16);
+            }
+        }
+        const uint32_t voff_sa = (uint32_t)(min(wave * 64 + lane, rows - 1) * p.sa_m * 4);
+        const uint32_t voff_sb = (uint32_t)(min(lane, C::kNB - 1) * p.sb_nb * 4);
 
-        auto load_stage = [&](int kb) {
+        auto issue = [&](int kb, int stage) {
+            const uint32_t sbase = smem_base + stage * C::kStageBytes;
 #pragma unroll
-            for (int q = 0; q < LA; ++q) {
-                const int c = q * kThreads + tid, row = c >> 3, ch = c & 7;
-                if (row < rows)
-                    ra[q] = *reinterpret_cast<const uint4 *>(Ab + (int64_t)row * p.lda + kb * 128 + ch * 16);
-                else
-                    ra[q] = make_uint4(0, 0, 0, 0);
+            for (int q = 0; q < SEGW; ++q) {
+                const int seg = q * C::kWaves + wave;
+                const uint8_t *base = (seg < C::kSegA ? Ab : Bb) + kb * 128;
+                dma_b128(base, voff[q], sbase + seg * 1024);
             }
-#pragma unroll
-            for (int q = 0; q < LB; ++q) {
-                const int c = q * kThreads + tid, row = c >> 3, ch = c & 7;
-                rb[q] = *reinterpret_cast<const uint4 *>(Bb + (int64_t)row * p.ldb + kb * 128 + ch * 16);
-            }
-            if (tid < BM)
-                rsa = (tid < rows) ? sAb[(int64_t)tid * p.sa_m + (int64_t)kb * p.sa_kb] : 0.f;
-        };
-        auto store_stage = [&](int s) {
-#pragma unroll
-            for (int q = 0; q < LA; ++q) {
-                const int c = q * kThreads + tid, row = c >> 3, ch = c & 7;
-                *reinterpret_cast<uint4 *>(&sm.a[s][lds_off(row, ch)]) = ra[q];
-            }
-#pragma unroll
-            for (int q = 0; q < LB; ++q) {
-                const int c = q * kThreads + tid, row = c >> 3, ch = c & 7;
-                *reinterpret_cast<uint4 *>(&sm.b[s][lds_off(row, ch)]) = rb[q];
-            }
-            if (tid < BM)
-                sm.sa[s][tid] = rsa;
+            if (loads_sa)
+                dma_b32(sAb + (int64_t)kb * p.sa_kb, voff_sa, sbase + C::kOffSa + wave * 256);
+            if (loads_sb)
+                dma_b32(sBb + (int64_t)kb * p.sb_kb, voff_sb, sbase + C::kOffSb);
         };
 
         v4f acc[MI][NJ];
@@ -239,39 +324,74 @@ __global__ void __launch_bounds__(kThreads) tile_kernel(Params p)
             for (int j = 0; j < NJ; ++j)
                 acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
 
-        __syncthreads();  // the previous tile's LDS reads are complete
-        load_stage(0);
-        float sb_cur = sBw[0];
-        store_stage(0);
-        __syncthreads();
-
-        for (int kb = 0; kb < nk; ++kb) {
-            const int cur = kb & 1;
-            const bool more = kb + 1 < nk;
-            float sb_next = 0.f;
-            if (more) {
-                load_stage(kb + 1);
-                sb_next = sBw[(int64_t)(kb + 1) * p.sb_kb];
-            }
+        // One K block on stage `st`: MFMA partials of sub-tile row i are
+        // issued while the VALU folds row i-1's partials into acc.
+        const bool wave_active = wm0 < rows;  // waves whose rows are all padding skip the math
+        auto compute = [&](auto stage_c) {
+            constexpr int st = decltype(stage_c)::value;
+            const uint8_t *As = smem + st * C::kStageBytes;
+            const uint8_t *Bs = As + C::kOffB;
+            const float *sas = reinterpret_cast<const float *>(As + C::kOffSa);
+            const float sb = reinterpret_cast<const float *>(As + C::kOffSb)[wn0 >> 7];
             v8i bf[NJ];
 #pragma unroll
             for (int j = 0; j < NJ; ++j)
-                bf[j] = lds_frag(sm.b[cur], wn0 + 16 * j + l16, lg);
+                bf[j] = lds_frag(Bs, wn0 + 16 * j + l16, lg);
+            v8i af = lds_frag(As, wm0 + l16, lg);
+            float sc = sas[wm0 + l16] * sb;
+            v4f part[NJ];
 #pragma unroll
-            for (int i = 0; i < MI; ++i) {
-                const int row = wm0 + 16 * i + l16;
-                const v8i af = lds_frag(sm.a[cur], row, lg);
-                const float s = sm.sa[cur][row] * sb_cur;
+            for (int j = 0; j < NJ; ++j)
+                part[j] = mfma_e4m3_16x16x128(bf[j], af);
+#pragma unroll
+            for (int i = 1; i < MI; ++i) {
+                const v8i afn = lds_frag(As, wm0 + 16 * i + l16, lg);
+                const float scn = sas[wm0 + 16 * i + l16] * sb;
 #pragma unroll
                 for (int j = 0; j < NJ; ++j) {
-                    const v4f part = mfma_e4m3_16x16x128(bf[j], af);
-                    acc[i][j] += part * s;
+                    const v4f nx = mfma_e4m3_16x16x128(bf[j], afn);
+                    acc[i - 1][j] += part[j] * sc;
+                    part[j] = nx;
                 }
+                sc = scn;
             }
-            if (more)
-                store_stage(cur ^ 1);
-            sb_cur = sb_next;
-            __syncthreads();
+#pragma unroll
+            for (int j = 0; j < NJ; ++j)
+                acc[MI - 1][j] += part[j] * sc;
+        };
+
+        // One pipeline step for K block kb held in stage st = kb % S.
+        auto step = [&](auto stage_c, int kb) {
+            constexpr int st = decltype(stage_c)::value;
+            // Stage kb has landed once at most (S-2) later stages are in flight.
+            if (kb + S - 2 < nk)
+                wait_stage<SEGW, S - 2>(per_stage);
+            else
+                wait_vmcnt<0>();
+            wg_barrier();  // every wave's DMA for kb is visible; stage (kb-1)%S is free
+            if (kb + S - 1 < nk)
+                issue(kb + S - 1, (st + S - 1) % S);
+            if (wave_active)
+                compute(stage_c);
+        };
+
+        // The previous tile's stores have completed (the vmcnt bookkeeping
+        // counts only this tile's DMA) and its LDS reads are done.
+        wait_vmcnt<0>();
+        wg_barrier();
+#pragma unroll
+        for (int s = 0; s < S - 1; ++s)
+            if (s < nk)
+                issue(s, s);
+
+        for (int kb0 = 0; kb0 < nk; kb0 += S) {
+            step(std::integral_constant<int, 0>{}, kb0);
+            if (kb0 + 1 < nk)
+                step(std::integral_constant<int, 1>{}, kb0 + 1);
+            if (S > 2 && kb0 + 2 < nk)
+                step(std::integral_constant<int, 2 % S>{}, kb0 + 2);
+            if (S > 3 && kb0 + 3 < nk)
+                step(std::integral_constant<int, 3 % S>{}, kb0 + 3);
         }
 
         uint16_t *Dg = p.D + (int64_t)g * p.d_stride_g;
@@ -284,7 +404,7 @@ __global__ void __launch_bounds__(kThreads) tile_kernel(Params p)
             else if (L == kMasked)
                 ok = m < limit;
             else
-                ok = p.ids[m] == expert;
+                ok = m < p.M && p.ids[m] == expert;
             if (!ok)
                 continue;
             uint16_t *drow = Dg + (int64_t)m * p.ldd + n0 + wn0 + 4 * lg;
@@ -297,24 +417,32 @@ __global__ void __launch_bounds__(kThreads) tile_kernel(Params p)
 
 // ---------------------------------------------------------------------------
 // Small-M kernel (decode shapes, M <= 16 * MT). One workgroup per 16 rows of
-// B; its four waves split the K blocks, read B straight from HBM into MFMA
-// operand registers (B is streamed exactly once, no LDS staging), and reduce
-// their fp32 accumulators through LDS at the end.
-constexpr int kDecodeUnroll = 8;  // K blocks whose loads are issued together
+// B; its eight waves split the K blocks, read B straight from HBM into MFMA
+// operand registers (B is streamed exactly once, no LDS staging) with every
+// load of a chunk issued before the first MFMA, and reduce their fp32
+// accumulators through LDS at the end in a fixed order.
+constexpr int kDecodeWaves = 8;
+constexpr int kDecodeThreads = kDecodeWaves * 64;
 
 template <int MT>
-__global__ void __launch_bounds__(kThreads) decode_kernel(Params p)
+struct DecodeCfg {
+    static constexpr int kUnroll = MT == 1 ? 8 : (MT == 2 ? 4 : 2);  // K blocks per load batch
+};
+
+template <int MT>
+__global__ void __launch_bounds__(kDecodeThreads, 1) decode_kernel(Params p)
 {
-    __shared__ v4f red[4][MT][64];
+    constexpr int U = DecodeCfg<MT>::kUnroll;
+    __shared__ v4f red[kDecodeWaves][MT][64];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6;
     const int l16 = lane & 15, lg = lane >> 4;
     const int n0 = blockIdx.x * 16;
     const int nk = p.K >> 7;
-    const int kb_begin = (wave * nk) >> 2, kb_end = ((wave + 1) * nk) >> 2;
+    const int kb_begin = (wave * nk) / kDecodeWaves, kb_end = ((wave + 1) * nk) / kDecodeWaves;
 
-    const uint8_t *brow = p.B + (int64_t)(n0 + l16) * p.ldb + 32 * lg;
+    const uint8_t *brow = p.B + (int64_t)(n0 + l16) * p.ldb + 16 * lg;
     const float *sbp = p.sB + (int64_t)(n0 >> 7) * p.sb_nb;
 
     v4f acc[MT];
@@ -322,29 +450,29 @@ __global__ void __launch_bounds__(kThreads) decode_kernel(Params p)
     for (int mt = 0; mt < MT; ++mt)
         acc[mt] = v4f{0.f, 0.f, 0.f, 0.f};
 
-    for (int kb0 = kb_begin; kb0 < kb_end; kb0 += kDecodeUnroll) {
-        v8i bf[kDecodeUnroll];
-        v8i af[kDecodeUnroll][MT];
-        float sb[kDecodeUnroll];
-        float sa[kDecodeUnroll][MT];
+    for (int kb0 = kb_begin; kb0 < kb_end; kb0 += U) {
+        v8i bf[U];
+        v8i af[U][MT];
+        float sb[U];
+        float sa[U][MT];
 #pragma unroll
-        for (int u = 0; u < kDecodeUnroll; ++u) {
+        for (int u = 0; u < U; ++u) {
             const int kb = kb0 + u;
             if (kb < kb_end) {
-                const uint4 *src = reinterpret_cast<const uint4 *>(brow + (int64_t)kb * 128);
-                bf[u] = join(src[0], src[1]);
+                const uint8_t *src = brow + (int64_t)kb * 128;
+                bf[u] = join(*reinterpret_cast<const uint4 *>(src), *reinterpret_cast<const uint4 *>(src + 64));
                 sb[u] = sbp[(int64_t)kb * p.sb_kb];
             }
         }
 #pragma unroll
-        for (int u = 0; u < kDecodeUnroll; ++u) {
+        for (int u = 0; u < U; ++u) {
             const int kb = kb0 + u;
 #pragma unroll
             for (int mt = 0; mt < MT; ++mt) {
                 const int m = mt * 16 + l16;
                 if (kb < kb_end && m < p.M) {
-                    const uint4 *src = reinterpret_cast<const uint4 *>(p.A + (int64_t)m * p.lda + (int64_t)kb * 128 + 32 * lg);
-                    af[u][mt] = join(src[0], src[1]);
+                    const uint8_t *src = p.A + (int64_t)m * p.lda + (int64_t)kb * 128 + 16 * lg;
+                    af[u][mt] = join(*reinterpret_cast<const uint4 *>(src), *reinterpret_cast<const uint4 *>(src + 64));
                     sa[u][mt] = p.sA[(int64_t)m * p.sa_m + (int64_t)kb * p.sa_kb];
                 } else {
                     af[u][mt] = v8i{0, 0, 0, 0, 0, 0, 0, 0};
@@ -353,7 +481,7 @@ __global__ void __launch_bounds__(kThreads) decode_kernel(Params p)
             }
         }
 #pragma unroll
-        for (int u = 0; u < kDecodeUnroll; ++u) {
+        for (int u = 0; u < U; ++u) {
             if (kb0 + u < kb_end) {
 #pragma unroll
                 for (int mt = 0; mt < MT; ++mt) {
@@ -368,9 +496,12 @@ __global__ void __launch_bounds__(kThreads) decode_kernel(Params p)
     for (int mt = 0; mt < MT; ++mt)
         red[wave][mt][lane] = acc[mt];
     __syncthreads();
-    // Wave w finishes m-subtiles mt = w, w + 4, ... in a fixed order (deterministic).
-    for (int mt = wave; mt < MT; mt += 4) {
-        const v4f v = ((red[0][mt][lane] + red[1][mt][lane]) + red[2][mt][lane]) + red[3][mt][lane];
+    // Wave w finishes m-subtiles mt = w, w + 8, ... summing the waves in order.
+    for (int mt = wave; mt < MT; mt += kDecodeWaves) {
+        v4f v = red[0][mt][lane];
+#pragma unroll
+        for (int w = 1; w < kDecodeWaves; ++w)
+            v += red[w][mt][lane];
         const int m = mt * 16 + l16;
         if (m < p.M)
             *reinterpret_cast<uint2 *>(p.D + (int64_t)m * p.ldd + n0 + 4 * lg) = pack_bf16x4(v);
