@@ -95,6 +95,9 @@ int64_t last_scale_index(int64_t rows, int64_t nkb, int64_t s_row, int64_t s_kb)
 // 8 waves (2 per SIMD) so one wave's promotion FMAs overlap another's MFMAs.
 using CfgDense = dgk::TileCfg<256, 128, 4, 2, 3, 4>;
 using CfgDense4 = dgk::TileCfg<256, 128, 2, 2, 3, 4>;
+using CfgBig = dgk::TileCfg<256, 256, 2, 4, 2, 4>;  // 2 stages of 66 KB; N % 256 == 0
+using CfgBigPP = dgk::TileCfg<256, 256, 2, 4, 2, 4, true>;
+using CfgDensePP = dgk::TileCfg<256, 128, 4, 2, 3, 4, true>;
 using CfgWide = dgk::TileCfg<128, 256, 2, 2, 3, 8>;
 using CfgNarrow = dgk::TileCfg<128, 128, 2, 2, 4, 8>;
 
@@ -111,6 +114,8 @@ int tile_override()
 template <int L, class C>
 int launch_tiles(dgk::Params &p, int groups, int cus, hipStream_t stream)
 {
+    if (p.N % C::kBN != 0)
+        return DG_ERR_UNSUPPORTED;  // every config is chosen so that its BN divides N
     p.tiles_m = (int)((p.M + C::kBM - 1) / C::kBM);
     p.tiles_n = p.N / C::kBN;
     const int64_t tiles = (int64_t)p.tiles_m * p.tiles_n * groups;
@@ -207,10 +212,17 @@ int dg_fp8_gemm_nt(const void *A, int64_t lda, const float *sA, int64_t sa_strid
         return launch_decode(p, s);
     if (!offsets_fit(lda, ldb, sa_stride_m))
         return DG_ERR_UNSUPPORTED;
+    const bool wide_n = N % 256 == 0;
     switch (tile_override()) {
     case 1: return launch_tiles<dgk::kDense, CfgDense4>(p, 1, dev.cus, s);
     case 2: return launch_tiles<dgk::kDense, CfgNarrow>(p, 1, dev.cus, s);
-    default: return launch_tiles<dgk::kDense, CfgDense>(p, 1, dev.cus, s);
+    case 4: return launch_tiles<dgk::kDense, CfgDense>(p, 1, dev.cus, s);
+    case 5: return wide_n ? launch_tiles<dgk::kDense, CfgBigPP>(p, 1, dev.cus, s) : DG_ERR_UNSUPPORTED;
+    case 6: return launch_tiles<dgk::kDense, CfgDensePP>(p, 1, dev.cus, s);
+    default:
+        if (wide_n)
+            return launch_tiles<dgk::kDense, CfgBig>(p, 1, dev.cus, s);
+        return launch_tiles<dgk::kDense, CfgDense>(p, 1, dev.cus, s);
     }
 }
 
@@ -315,7 +327,11 @@ int dg_fp8_grouped_gemm_masked(const void *A, int64_t lda, int64_t a_stride_g, c
     switch (tile_override()) {
     case 1: return launch_tiles<dgk::kMasked, CfgDense4>(p, (int)G, dev.cus, (hipStream_t)stream);
     case 2: return launch_tiles<dgk::kMasked, CfgNarrow>(p, (int)G, dev.cus, (hipStream_t)stream);
-    default: return launch_tiles<dgk::kMasked, CfgDense>(p, (int)G, dev.cus, (hipStream_t)stream);
+    case 4: return launch_tiles<dgk::kMasked, CfgDense>(p, (int)G, dev.cus, (hipStream_t)stream);
+    default:
+        if (N % 256 == 0)
+            return launch_tiles<dgk::kMasked, CfgBig>(p, (int)G, dev.cus, (hipStream_t)stream);
+        return launch_tiles<dgk::kMasked, CfgDense>(p, (int)G, dev.cus, (hipStream_t)stream);
     }
 }
 
