@@ -140,7 +140,40 @@ int launch_decode(dgk::Params &p, hipStream_t stream)
 {
     const int grid = p.N / 16;
     hipError_t e;
-    if (p.M <= 16)
+    const int64_t nkb = p.K / 128;
+    if (p.M <= 8 && nkb % dgk::kDecodeWaves == 0 && nkb / dgk::kDecodeWaves <= 8 && tile_override() < 7 &&
+        (int64_t)(p.M - 1) * p.lda + p.K < ((int64_t)1 << 31) &&
+        ((int64_t)(p.M - 1) * p.sa_m + (nkb - 1) * p.sa_kb) * 4 < ((int64_t)1 << 31)) {
+        const dim3 g(grid), b(dgk::kDecodeThreads);
+        const bool full = tile_override() != 6;
+        switch (nkb / dgk::kDecodeWaves) {
+        case 1: if (full) hipLaunchKernelGGL((dgk::decode_dma_kernel<1, 8, true>), g, b, 0, stream, p); else hipLaunchKernelGGL((dgk::decode_dma_kernel<1, 8, false>), g, b, 0, stream, p); break;
+        case 2: if (full) hipLaunchKernelGGL((dgk::decode_dma_kernel<2, 8, true>), g, b, 0, stream, p); else hipLaunchKernelGGL((dgk::decode_dma_kernel<2, 8, false>), g, b, 0, stream, p); break;
+        case 3: if (full) hipLaunchKernelGGL((dgk::decode_dma_kernel<3, 8, true>), g, b, 0, stream, p); else hipLaunchKernelGGL((dgk::decode_dma_kernel<3, 8, false>), g, b, 0, stream, p); break;
+        case 4: if (full) hipLaunchKernelGGL((dgk::decode_dma_kernel<4, 8, true>), g, b, 0, stream, p); else hipLaunchKernelGGL((dgk::decode_dma_kernel<4, 8, false>), g, b, 0, stream, p); break;
+        case 5: if (full) hipLaunchKernelGGL((dgk::decode_dma_kernel<5, 8, true>), g, b, 0, stream, p); else hipLaunchKernelGGL((dgk::decode_dma_kernel<5, 8, false>), g, b, 0, stream, p); break;
+        case 6: if (full) hipLaunchKernelGGL((dgk::decode_dma_kernel<6, 8, true>), g, b, 0, stream, p); else hipLaunchKernelGGL((dgk::decode_dma_kernel<6, 8, false>), g, b, 0, stream, p); break;
+        case 7: if (full) hipLaunchKernelGGL((dgk::decode_dma_kernel<7, 8, true>), g, b, 0, stream, p); else hipLaunchKernelGGL((dgk::decode_dma_kernel<7, 8, false>), g, b, 0, stream, p); break;
+        default: if (full) hipLaunchKernelGGL((dgk::decode_dma_kernel<8, 8, true>), g, b, 0, stream, p); else hipLaunchKernelGGL((dgk::decode_dma_kernel<8, 8, false>), g, b, 0, stream, p); break;
+        }
+    } else if (p.M <= 16 && nkb % dgk::kDecodeWaves == 0 && nkb / dgk::kDecodeWaves <= 8 && tile_override() != 7 &&
+        tile_override() != 8) {
+        const dim3 g(grid), b(dgk::kDecodeThreads);
+        switch (nkb / dgk::kDecodeWaves) {
+        case 1: hipLaunchKernelGGL(dgk::decode_static_kernel<1>, g, b, 0, stream, p); break;
+        case 2: hipLaunchKernelGGL(dgk::decode_static_kernel<2>, g, b, 0, stream, p); break;
+        case 3: hipLaunchKernelGGL(dgk::decode_static_kernel<3>, g, b, 0, stream, p); break;
+        case 4: hipLaunchKernelGGL(dgk::decode_static_kernel<4>, g, b, 0, stream, p); break;
+        case 5: hipLaunchKernelGGL(dgk::decode_static_kernel<5>, g, b, 0, stream, p); break;
+        case 6: hipLaunchKernelGGL(dgk::decode_static_kernel<6>, g, b, 0, stream, p); break;
+        case 7: hipLaunchKernelGGL(dgk::decode_static_kernel<7>, g, b, 0, stream, p); break;
+        default: hipLaunchKernelGGL(dgk::decode_static_kernel<8>, g, b, 0, stream, p); break;
+        }
+    } else if (p.M <= 16 && (int64_t)p.M * p.K <= dgk::kDecodeLdsA && (int64_t)p.M * nkb <= dgk::kDecodeLdsSa &&
+        ((int64_t)p.M * p.K) % 1024 == 0 && (int64_t)(p.M - 1) * p.lda + p.K < ((int64_t)1 << 31) &&
+        ((int64_t)(p.M - 1) * p.sa_m + (nkb - 1) * p.sa_kb) * 4 < ((int64_t)1 << 31) && tile_override() != 7)
+        hipLaunchKernelGGL(dgk::decode_lds_kernel, dim3(grid), dim3(dgk::kDecodeThreads), 0, stream, p);
+    else if (p.M <= 16)
         hipLaunchKernelGGL(dgk::decode_kernel<1>, dim3(grid), dim3(dgk::kDecodeThreads), 0, stream, p);
     else if (p.M <= 32)
         hipLaunchKernelGGL(dgk::decode_kernel<2>, dim3(grid), dim3(dgk::kDecodeThreads), 0, stream, p);
@@ -208,7 +241,7 @@ int dg_fp8_gemm_nt(const void *A, int64_t lda, const float *sA, int64_t sa_strid
     p.D = (uint16_t *)D; p.ldd = ldd;
     p.M = (int)M; p.N = (int)N; p.K = (int)K; p.G = 1;
     hipStream_t s = (hipStream_t)stream;
-    if (M <= 64 && tile_override() < 0)
+    if (M <= 64 && (tile_override() < 0 || tile_override() >= 7))
         return launch_decode(p, s);
     if (!offsets_fit(lda, ldb, sa_stride_m))
         return DG_ERR_UNSUPPORTED;

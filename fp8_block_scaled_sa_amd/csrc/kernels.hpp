@@ -664,4 +664,297 @@ __global__ void __launch_bounds__(kDecodeThreads, 1) decode_kernel(Params p)
     }
 }
 
+// ---------------------------------------------------------------------------
+// Small-M kernel with the whole LHS staged in LDS (M <= 16 and M*K bytes
+// within kDecodeLdsA): the decode-shaped case, bound by streaming B once.
+// Per workgroup (16 rows of B, eight waves splitting the K blocks):
+//   1. every wave issues the non-temporal loads of its B blocks first (the
+//      long pole, HBM), then its share of the LDS-DMA of A and sA (served
+//      by L2, shared by all workgroups), then one load of its sB values;
+//   2. one wait and one barrier, then MFMA + promotion per block from
+//      registers (B) and LDS (A, sA); sB is broadcast from its lane;
+//   3. fixed-order reduction of the eight waves through LDS, bf16 store.
+constexpr int kDecodeLdsA = 120 * 1024;   // LHS bytes held in LDS
+constexpr int kDecodeLdsSa = 1024;        // LHS scales (floats) held in LDS
+constexpr int kDecodeLdsUnroll = 8;       // B blocks per wave held in registers per pass
+
+__device__ __forceinline__ v8i load_nt_b256(const uint8_t *p)
+{
+    typedef unsigned int v4u __attribute__((ext_vector_type(4)));
+    const v4u lo = __builtin_nontemporal_load(reinterpret_cast<const v4u *>(p));
+    const v4u hi = __builtin_nontemporal_load(reinterpret_cast<const v4u *>(p + 64));
+    v8i r;
+    r[0] = (int)lo[0]; r[1] = (int)lo[1]; r[2] = (int)lo[2]; r[3] = (int)lo[3];
+    r[4] = (int)hi[0]; r[5] = (int)hi[1]; r[6] = (int)hi[2]; r[7] = (int)hi[3];
+    return r;
+}
+
+__global__ void __launch_bounds__(kDecodeThreads, 1) decode_lds_kernel(Params p)
+{
+    __shared__ __attribute__((aligned(1024))) uint8_t a_lds[kDecodeLdsA];
+    __shared__ float sa_lds[kDecodeLdsSa];
+    __shared__ v4f red[kDecodeWaves][64];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int l16 = lane & 15, lg = lane >> 4;
+    const int n0 = blockIdx.x * 16;
+    const int nk = p.K >> 7;
+    const int M = p.M;
+    const int kb_begin = (wave * nk) / kDecodeWaves, kb_end = ((wave + 1) * nk) / kDecodeWaves;
+
+    const uint8_t *brow = p.B + (int64_t)(n0 + l16) * p.ldb + 16 * lg;
+    const float *sbp = p.sB + (int64_t)(n0 >> 7) * p.sb_nb;
+    const uint32_t a_base = lds_addr(a_lds), sa_base = lds_addr(sa_lds);
+    const v4i rsrc_a = buffer_rsrc(p.A, (uint32_t)((int64_t)(M - 1) * p.lda + p.K));
+
+    v4f acc = {0.f, 0.f, 0.f, 0.f};
+    bool staged = false;
+    for (int kb0 = kb_begin; kb0 < kb_end || !staged; kb0 += kDecodeLdsUnroll) {
+        v8i bf[kDecodeLdsUnroll];
+#pragma unroll
+        for (int u = 0; u < kDecodeLdsUnroll; ++u)
+            if (kb0 + u < kb_end)
+                bf[u] = load_nt_b256(brow + (int64_t)(kb0 + u) * 128);
+        if (!staged) {
+            // LHS rows [0, M) -> LDS as M rows of K bytes, 1 KB per DMA op.
+            const int a_ops = (M * p.K) >> 10;
+            for (int q = wave; q < a_ops; q += kDecodeWaves) {
+                const int b = (q << 10) + 16 * lane;     // byte in the LDS image
+                const int row = b / p.K, col = b - row * p.K;
+                dma_buf_b128(rsrc_a, (uint32_t)(row * p.lda + col), 0u, a_base + (q << 10));
+            }
+            const int sa_ops = (M * nk + 63) >> 6;
+            for (int q = wave; q < sa_ops; q += kDecodeWaves) {
+                int e = (q << 6) + lane;
+                e = e < M * nk ? e : 0;
+                const int m = e / nk, kb = e - m * nk;
+                dma_b32(p.sA, (uint32_t)((m * p.sa_m + kb * p.sa_kb) * 4), sa_base + (q << 8));
+            }
+        }
+        // This wave's sB values, one per lane, broadcast per block below.
+        const int cnt = min(kDecodeLdsUnroll, kb_end - kb0);
+        const float sbv = cnt > 0 ? sbp[(int64_t)(kb0 + min(lane, cnt - 1)) * p.sb_kb] : 0.f;
+        wait_vmcnt<0>();
+        if (!staged) {
+            wg_barrier();  // A and sA are in LDS for every wave
+            staged = true;
+        }
+#pragma unroll
+        for (int u = 0; u < kDecodeLdsUnroll; ++u) {
+            const int kb = kb0 + u;
+            if (kb < kb_end) {
+                v8i af = v8i{0, 0, 0, 0, 0, 0, 0, 0};
+                float sa = 0.f;
+                if (l16 < M) {
+                    const uint8_t *ar = a_lds + l16 * p.K + kb * 128 + 16 * lg;
+                    af = join(*reinterpret_cast<const uint4 *>(ar), *reinterpret_cast<const uint4 *>(ar + 64));
+                    sa = sa_lds[l16 * nk + kb];
+                }
+                const float sb = __shfl(sbv, u);
+                const v4f part = mfma_e4m3_16x16x128(bf[u], af);
+                acc += part * (sa * sb);
+            }
+        }
+    }
+
+    red[wave][lane] = acc;
+    __syncthreads();
+    if (wave == 0) {
+        v4f v = red[0][lane];
+#pragma unroll
+        for (int w = 1; w < kDecodeWaves; ++w)
+            v += red[w][lane];
+        if (l16 < M)
+            *reinterpret_cast<uint2 *>(p.D + (int64_t)l16 * p.ldd + n0 + 4 * lg) = pack_bf16x4(v);
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Small-M kernel with a fixed number of K blocks per wave (M <= 16, K =
+// 8 * NB * 128): every load is unconditional and issued up front in block
+// order (A fragments and sA first, they come from L2; then sB; then B, the
+// HBM stream), so the compiler waits for each block's B alone and the MFMA
+// and promotion of block u run while blocks u+1.. are still in flight. Only
+// the last block's math and the cross-wave reduction follow the last byte.
+template <int NB>
+__global__ void __launch_bounds__(kDecodeThreads, 1) decode_static_kernel(Params p)
+{
+    __shared__ v4f red[kDecodeWaves][64];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, wave = tid >> 6;
+    const int l16 = lane & 15, lg = lane >> 4;
+    const int n0 = blockIdx.x * 16;
+    const int kb0 = wave * NB;
+    const bool arow = l16 < p.M;
+
+    const uint8_t *arow_p = p.A + (int64_t)l16 * p.lda + (int64_t)kb0 * 128 + 16 * lg;
+    const float *sarow_p = p.sA + (int64_t)l16 * p.sa_m + (int64_t)kb0 * p.sa_kb;
+    v8i af[NB];
+    float sa[NB];
+#pragma unroll
+    for (int u = 0; u < NB; ++u) {
+        if (arow) {
+            const uint8_t *src = arow_p + u * 128;
+            af[u] = join(*reinterpret_cast<const uint4 *>(src), *reinterpret_cast<const uint4 *>(src + 64));
+            sa[u] = sarow_p[(int64_t)u * p.sa_kb];
+        } else {
+            af[u] = v8i{0, 0, 0, 0, 0, 0, 0, 0};
+            sa[u] = 0.f;
+        }
+    }
+    const float *sbp = p.sB + (int64_t)(n0 >> 7) * p.sb_nb + (int64_t)kb0 * p.sb_kb;
+    const float sbv = sbp[(int64_t)min(lane, NB - 1) * p.sb_kb];
+
+    const uint8_t *brow = p.B + (int64_t)(n0 + l16) * p.ldb + (int64_t)kb0 * 128 + 16 * lg;
+    v8i bf[NB];
+#pragma unroll
+    for (int u = 0; u < NB; ++u) {
+        const uint8_t *src = brow + u * 128;
+        bf[u] = join(*reinterpret_cast<const uint4 *>(src), *reinterpret_cast<const uint4 *>(src + 64));
+    }
+    // Keep every load above this point: the scheduler would otherwise sink
+    // later loads below earlier MFMAs to save registers, serialising latency.
+    __builtin_amdgcn_sched_barrier(0);
+
+    v4f acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int u = 0; u < NB; ++u) {
+        const float sb = __shfl(sbv, u);
+        const v4f part = mfma_e4m3_16x16x128(bf[u], af[u]);
+        acc += part * (sa[u] * sb);
+    }
+
+    red[wave][lane] = acc;
+    __syncthreads();
+    if (wave == 0) {
+        v4f v = red[0][lane];
+#pragma unroll
+        for (int w = 1; w < kDecodeWaves; ++w)
+            v += red[w][lane];
+        if (arow)
+            *reinterpret_cast<uint2 *>(p.D + (int64_t)l16 * p.ldd + n0 + 4 * lg) = pack_bf16x4(v);
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Small-M kernel, M <= MR (8 or 16), NB K blocks per wave (K = 8 * NB * 128).
+// Each wave stages the LHS rows of its own K blocks (and their sA) in a
+// wave-private LDS region with full-line LDS-DMA, issued first; then it loads
+// sB and issues its B blocks (the HBM stream) straight into MFMA operand
+// registers. No barrier precedes the math: a wave only reads its own LDS
+// region, and each block's MFMA waits for that block's B alone.
+template <int NB, int MR, bool BFULL>
+__global__ void __launch_bounds__(kDecodeThreads, 1) decode_dma_kernel(Params p)
+{
+    static_assert(MR == 8 || MR == 16, "LHS rows staged per block");
+    constexpr int kBlk = MR * 128;                 // LDS bytes per K block of the LHS
+    constexpr int kOps = NB * MR / 8;              // 1 KB DMA ops per wave for the LHS
+    static_assert(MR * NB <= 64, "one dword DMA op carries a wave's sA");
+    __shared__ __attribute__((aligned(1024))) uint8_t a_lds[kDecodeWaves][NB * kBlk];
+    __shared__ __attribute__((aligned(1024))) uint8_t b_ring[kDecodeWaves][BFULL ? 2 : 1][2048];
+    __shared__ float sa_lds[kDecodeWaves][64];
+    __shared__ v4f red[kDecodeWaves][64];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int l16 = lane & 15, lg = lane >> 4;
+    const int n0 = blockIdx.x * 16;
+    const int kb0 = wave * NB;
+    const int M = p.M;
+
+    // 1. LHS: op q covers rows 8(q%(MR/8))..+7 of block q/(MR/8); lane i takes
+    // row +i/8, physical chunk i%8 = logical chunk (i%8) ^ swz(row).
+    const uint32_t a_base = lds_addr(&a_lds[wave][0]);
+    const v4i rsrc_a = buffer_rsrc(p.A, (uint32_t)((int64_t)(M - 1) * p.lda + p.K));
+#pragma unroll
+    for (int q = 0; q < kOps; ++q) {
+        const int u = q / (MR / 8), r = (q % (MR / 8)) * 8 + (lane >> 3);
+        const int ch = (lane & 7) ^ swz(r);
+        const uint32_t voff = r < M ? (uint32_t)(r * p.lda + (kb0 + u) * 128 + ch * 16) : 0xffffffffu;
+        dma_buf_b128(rsrc_a, voff, 0u, a_base + q * 1024);
+    }
+    {   // sA for (row, block) = (lane % MR, lane / MR)
+        const int r = lane % MR, u = min(lane / MR, NB - 1);
+        const int rr = r < M ? r : 0;
+        dma_b32(p.sA, (uint32_t)((rr * p.sa_m + (int64_t)(kb0 + u) * p.sa_kb) * 4), lds_addr(&sa_lds[wave][0]));
+    }
+    // 2. sB for the wave's blocks, one per lane.
+    const float *sbp = p.sB + (int64_t)(n0 >> 7) * p.sb_nb + (int64_t)kb0 * p.sb_kb;
+    const float sbv = sbp[(int64_t)min(lane, NB - 1) * p.sb_kb];
+    // 3. B blocks. BFULL: non-temporal full 128-byte lines (lane i: row
+    // 8 j + i/8, chunk i%8 of instruction j), transposed to the MFMA layout
+    // through a two-slot wave-private LDS ring; otherwise straight into MFMA
+    // operand registers (16 rows x 64 bytes per instruction).
+    typedef unsigned int v4u __attribute__((ext_vector_type(4)));
+    v4u bl[NB][2];
+    v8i bf[NB];
+    if constexpr (BFULL) {
+        const uint8_t *bbase = p.B + (int64_t)(n0 + (lane >> 3)) * p.ldb + (int64_t)kb0 * 128 + 16 * (lane & 7);
+#pragma unroll
+        for (int u = 0; u < NB; ++u) {
+#pragma unroll
+            for (int j = 0; j < 2; ++j)
+                bl[u][j] = __builtin_nontemporal_load(
+                    reinterpret_cast<const v4u *>(bbase + (int64_t)(8 * j) * p.ldb + u * 128));
+            __builtin_amdgcn_sched_barrier(0);  // keep block order: each block waits for itself only
+        }
+    } else {
+        const uint8_t *brow = p.B + (int64_t)(n0 + l16) * p.ldb + (int64_t)kb0 * 128 + 16 * lg;
+#pragma unroll
+        for (int u = 0; u < NB; ++u) {
+            const uint8_t *src = brow + u * 128;
+            bf[u] = join(*reinterpret_cast<const uint4 *>(src), *reinterpret_cast<const uint4 *>(src + 64));
+        }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    // The LHS DMA is older than sB and the B loads: it has landed once at most
+    // 1 + 2 NB loads are outstanding.
+    wait_vmcnt<1 + 2 * NB>();
+
+    v4f acc = {0.f, 0.f, 0.f, 0.f};
+    const bool arow = l16 < M;
+    const int fsw = swz(l16);
+    const int fsw_a = swz(l16 & 7);
+#pragma unroll
+    for (int u = 0; u < NB; ++u) {
+        if constexpr (BFULL) {
+            uint8_t *slot = &b_ring[wave][u & 1][0];
+#pragma unroll
+            for (int j = 0; j < 2; ++j) {
+                const int r = 8 * j + (lane >> 3);
+                *reinterpret_cast<v4u *>(slot + r * 128 + (((lane & 7) ^ swz(r)) << 4)) = bl[u][j];
+            }
+            const uint8_t *t = slot + l16 * 128;
+            bf[u] = join(*reinterpret_cast<const uint4 *>(t + ((lg ^ fsw) << 4)),
+                         *reinterpret_cast<const uint4 *>(t + (((lg + 4) ^ fsw) << 4)));
+        }
+        v8i af = v8i{0, 0, 0, 0, 0, 0, 0, 0};
+        float sa = 0.f;
+        if (arow) {
+            const uint8_t *t = &a_lds[wave][u * kBlk + l16 * 128];
+            af = join(*reinterpret_cast<const uint4 *>(t + ((lg ^ fsw_a) << 4)),
+                      *reinterpret_cast<const uint4 *>(t + (((lg + 4) ^ fsw_a) << 4)));
+            sa = sa_lds[wave][u * MR + l16];
+        }
+        const float sb = __shfl(sbv, u);
+        const v4f part = mfma_e4m3_16x16x128(bf[u], af);
+        acc += part * (sa * sb);
+    }
+
+    red[wave][lane] = acc;
+    __syncthreads();
+    if (wave == 0) {
+        v4f v = red[0][lane];
+#pragma unroll
+        for (int w = 1; w < kDecodeWaves; ++w)
+            v += red[w][lane];
+        if (arow)
+            *reinterpret_cast<uint2 *>(p.D + (int64_t)l16 * p.ldd + n0 + 4 * lg) = pack_bf16x4(v);
+    }
+}
+
 }  // namespace dgk
