@@ -96,9 +96,6 @@ int64_t last_scale_index(int64_t rows, int64_t nkb, int64_t s_row, int64_t s_kb)
 using CfgDense = dgk::TileCfg<256, 128, 4, 2, 3, 4>;
 using CfgDense4 = dgk::TileCfg<256, 128, 2, 2, 3, 4>;
 using CfgBig = dgk::TileCfg<256, 256, 2, 4, 2, 4>;  // 2 stages of 66 KB; N % 256 == 0
-using CfgBigPP = dgk::TileCfg<256, 256, 2, 4, 2, 4, 1>;
-using CfgDensePP = dgk::TileCfg<256, 128, 4, 2, 3, 4, 1>;
-using CfgDenseRP = dgk::TileCfg<256, 128, 4, 2, 3, 4, 2>;  // register prefetch
 using CfgWide = dgk::TileCfg<128, 256, 2, 2, 3, 8>;
 using CfgNarrow = dgk::TileCfg<128, 128, 2, 2, 4, 8>;
 
@@ -251,9 +248,6 @@ int dg_fp8_gemm_nt(const void *A, int64_t lda, const float *sA, int64_t sa_strid
     case 1: return launch_tiles<dgk::kDense, CfgDense4>(p, 1, dev.cus, s);
     case 2: return launch_tiles<dgk::kDense, CfgNarrow>(p, 1, dev.cus, s);
     case 4: return launch_tiles<dgk::kDense, CfgDense>(p, 1, dev.cus, s);
-    case 5: return wide_n ? launch_tiles<dgk::kDense, CfgBigPP>(p, 1, dev.cus, s) : DG_ERR_UNSUPPORTED;
-    case 6: return launch_tiles<dgk::kDense, CfgDensePP>(p, 1, dev.cus, s);
-    case 10: return launch_tiles<dgk::kDense, CfgDenseRP>(p, 1, dev.cus, s);
     default:
         if (wide_n)
             return launch_tiles<dgk::kDense, CfgBig>(p, 1, dev.cus, s);

@@ -210,13 +210,9 @@ __device__ __forceinline__ void tile_coords(int t, int tiles_m, int tiles_n, int
 // columns must lie in one 128-wide sB block), WAVES_M x WAVES_N waves, each
 // owning a (BM/WAVES_M) x (BN/WAVES_N) block of 16x16 sub-tiles. STAGES LDS
 // buffers, each holding one K block of the A tile, the B tile and sA.
-template <int BM, int BN, int WAVES_M, int WAVES_N, int STAGES, int GROUP_M, int SCHED = 0>
+template <int BM, int BN, int WAVES_M, int WAVES_N, int STAGES, int GROUP_M>
 struct TileCfg {
     static constexpr int kBM = BM, kBN = BN, kStages = STAGES, kGroupM = GROUP_M;
-    // K-loop schedule: 0 = LDS fragments read per step, 1 = ping-pong wave
-    // groups, 2 = fragments of step k+1 read into registers during step k.
-    static constexpr int kSched = SCHED;
-    static constexpr bool kPingPong = SCHED == 1;
     static constexpr int kWavesM = WAVES_M, kWavesN = WAVES_N;
     static constexpr int kWaves = WAVES_M * WAVES_N;
     static constexpr int kThreads = kWaves * 64;
@@ -237,8 +233,6 @@ struct TileCfg {
     static_assert(STAGES >= 2 && STAGES <= 4, "pipeline depth (the K loop is unrolled by at most 4)");
     static_assert(kSmemBytes <= 160 * 1024, "LDS");
     static_assert((kSegPerWave + 2) * (STAGES - 2) < 64, "vmcnt range");
-    static_assert(SCHED != 1 || (kWaves == 8 && kMI % 2 == 0), "ping-pong: two groups of four waves, split rows");
-    static_assert(SCHED != 2 || STAGES == 2 || STAGES == 3, "register prefetch unrolls the K loop by 6");
 };
 
 // Wait until this wave's DMA for the oldest pipeline stage has landed: at most
@@ -366,57 +360,69 @@ __global__ void __launch_bounds__(C::kThreads, 1) tile_kernel(Params p)
         const int fa_lo = (wm0 + l16) * 128 + ((lg ^ fsw) << 4), fa_hi = (wm0 + l16) * 128 + (((lg + 4) ^ fsw) << 4);
         const int fb_lo = (wn0 + l16) * 128 + ((lg ^ fsw) << 4), fb_hi = (wn0 + l16) * 128 + (((lg + 4) ^ fsw) << 4);
 
-        // One K block on stage `st`: MFMA partials of sub-tile row i are
-        // issued while the VALU folds row i-1's partials into acc.
+        // The rows of MFMA partials form one stream across K blocks: row i's
+        // partials are folded into acc (times sA * sB of their block) while
+        // the MFMAs of the next row run, and the last row of a block is
+        // folded during row 0 of the next block, so the matrix core is not
+        // left idle around the block barrier waiting for a promotion.
+        v4f part[NJ];
+#pragma unroll
+        for (int j = 0; j < NJ; ++j)
+            part[j] = v4f{0.f, 0.f, 0.f, 0.f};
+        float part_sc = 0.f;   // scale of the row held in part
+
         const bool wave_active = wm0 < rows;  // waves whose rows are all padding skip the math
         auto compute = [&](auto stage_c) {
             constexpr int st = decltype(stage_c)::value;
             const uint8_t *As = smem + st * C::kStageBytes;
             const uint8_t *Bs = As + C::kOffB;
             const float *sas = reinterpret_cast<const float *>(As + C::kOffSa);
-            const float sb = reinterpret_cast<const float *>(As + C::kOffSb)[wn0 >> 7];
             auto frag = [&](const uint8_t *t, int lo, int hi, int k) {
                 return join(*reinterpret_cast<const uint4 *>(t + lo + 2048 * k),
                             *reinterpret_cast<const uint4 *>(t + hi + 2048 * k));
             };
-            // The A fragment of row i+1 is read before the MFMAs of row i
-            // (two fragment registers in flight), so the matrix core never
-            // waits for LDS behind its own operand registers; each row's
-            // MFMAs are interleaved one-to-four with the promotion FMAs of
-            // the previous row, whose partials are long complete.
-            v8i bf[NJ];
-#pragma unroll
-            for (int j = 0; j < NJ; ++j)
-                bf[j] = frag(Bs, fb_lo, fb_hi, j);
-            float sc[MI];
-#pragma unroll
-            for (int i = 0; i < MI; ++i)
-                sc[i] = sas[wm0 + 16 * i + l16];
-            v8i af[2];
+            // LDS reads in the order the MFMAs consume them (in-order
+            // completion lets each MFMA wait for just its own operands): A
+            // row 0, the B fragments, A row 1, then the scales, which only
+            // the promotions need.
+            v8i af[2], bf[NJ];
             af[0] = frag(As, fa_lo, fa_hi, 0);
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int j = 0; j < NJ; ++j) {
+                bf[j] = frag(Bs, fb_lo, fb_hi, j);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+            if (MI > 1)
+                af[1] = frag(As, fa_lo, fa_hi, 1);
+            __builtin_amdgcn_sched_barrier(0);
+            const float sb = reinterpret_cast<const float *>(As + C::kOffSb)[wn0 >> 7];
+            float sa[MI];
 #pragma unroll
             for (int i = 0; i < MI; ++i)
-                sc[i] *= sb;
-            v4f part[NJ];
+                sa[i] = sas[wm0 + 16 * i + l16];
+            __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
             for (int i = 0; i < MI; ++i) {
-                if (i + 1 < MI)
+                if (i >= 1 && i + 1 < MI)
                     af[(i + 1) & 1] = frag(As, fa_lo, fa_hi, i + 1);
                 __builtin_amdgcn_sched_barrier(0);
+                // part holds row i-1 (the previous block's last row when i == 0)
+                const float sc = part_sc;
 #pragma unroll
                 for (int j = 0; j < NJ; ++j) {
                     const v4f nx = mfma_e4m3_16x16x128(bf[j], af[i & 1]);
-                    if (i > 0)
-                        acc[i - 1][j] += part[j] * sc[i - 1];
+                    if (i == 0)
+                        acc[MI - 1][j] += part[j] * sc;
+                    else
+                        acc[i - 1][j] += part[j] * sc;
                     part[j] = nx;
                     __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
                     __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);  // four VALU
                 }
                 __builtin_amdgcn_sched_barrier(0);
+                part_sc = sa[i] * sb;
             }
-#pragma unroll
-            for (int j = 0; j < NJ; ++j)
-                acc[MI - 1][j] += part[j] * sc[MI - 1];
         };
 
         // One pipeline step for K block kb held in stage st = kb % S.
@@ -438,234 +444,23 @@ __global__ void __launch_bounds__(C::kThreads, 1) tile_kernel(Params p)
         // counts only this tile's DMA) and its LDS reads are done.
         wait_vmcnt<0>();
         wg_barrier();
-        if constexpr (C::kSched != 2) {
 #pragma unroll
-            for (int s = 0; s < S - 1; ++s)
-                if (s < nk)
-                    issue(s, s);
+        for (int s = 0; s < S - 1; ++s)
+            if (s < nk)
+                issue(s, s);
+        for (int kb0 = 0; kb0 < nk; kb0 += S) {
+            step(std::integral_constant<int, 0>{}, kb0);
+            if (kb0 + 1 < nk)
+                step(std::integral_constant<int, 1 % S>{}, kb0 + 1);
+            if (S > 2 && kb0 + 2 < nk)
+                step(std::integral_constant<int, 2 % S>{}, kb0 + 2);
+            if (S > 3 && kb0 + 3 < nk)
+                step(std::integral_constant<int, 3 % S>{}, kb0 + 3);
         }
-
-        if constexpr (C::kSched == 2) {
-            // Register prefetch. Step j computes from fragments already in
-            // VGPRs (set j%2) while its LDS reads fetch step j+1's fragments
-            // (set (j+1)%2) from stage (j+1)%S, so MFMAs never wait on LDS.
-            // DMA for block j+S goes into stage j%S, which every wave left
-            // during step j-1 (the barrier of step j guarantees it).
-            v8i fb[2][NJ], fa[2][MI];
-            float fsc[2][MI];
-            auto frag = [&](const uint8_t *t, int lo, int hi, int k) {
-                return join(*reinterpret_cast<const uint4 *>(t + lo + 2048 * k),
-                            *reinterpret_cast<const uint4 *>(t + hi + 2048 * k));
-            };
-            auto fetch_b = [&](auto stage_c, auto set_c) {
-                constexpr int st = decltype(stage_c)::value, fs = decltype(set_c)::value;
-                const uint8_t *Bs = smem + st * C::kStageBytes + C::kOffB;
+        // fold the last row
 #pragma unroll
-                for (int j = 0; j < NJ; ++j)
-                    fb[fs][j] = frag(Bs, fb_lo, fb_hi, j);
-            };
-            auto fetch_a = [&](auto stage_c, auto set_c, int i) {
-                constexpr int st = decltype(stage_c)::value, fs = decltype(set_c)::value;
-                const uint8_t *As = smem + st * C::kStageBytes;
-                const float sb = reinterpret_cast<const float *>(As + C::kOffSb)[wn0 >> 7];
-                fa[fs][i] = frag(As, fa_lo, fa_hi, i);
-                fsc[fs][i] = reinterpret_cast<const float *>(As + C::kOffSa)[wm0 + 16 * i + l16] * sb;
-            };
-
-#pragma unroll
-            for (int s = 0; s < S; ++s)
-                if (s < nk)
-                    issue(s, s);
-            if (S - 1 <= nk - 1)
-                wait_stage<SEGW, S - 1>(per_stage);
-            else
-                wait_vmcnt<0>();
-            wg_barrier();
-            using Z = std::integral_constant<int, 0>;
-            fetch_b(Z{}, Z{});
-#pragma unroll
-            for (int i = 0; i < MI; ++i)
-                fetch_a(Z{}, Z{}, i);
-
-            auto pstep = [&](auto stage_c, auto set_c, int j) {
-                constexpr int st = decltype(stage_c)::value, fs = decltype(set_c)::value;
-                using Next = std::integral_constant<int, (st + 1) % S>;
-                using NSet = std::integral_constant<int, fs ^ 1>;
-                if (j + 1 < nk) {
-                    if (j + S - 1 < nk)
-                        wait_stage<SEGW, S - 2>(per_stage);
-                    else
-                        wait_vmcnt<0>();
-                    wg_barrier();
-                }
-                if (j + S < nk)
-                    issue(j + S, st);
-                // Next step's fragments are read unconditionally (past the
-                // last block they re-read a stage in bounds and go unused).
-                fetch_b(Next{}, NSet{});
-                if (wave_active) {
-                    v4f part[NJ];
-#pragma unroll
-                    for (int jj = 0; jj < NJ; ++jj)
-                        part[jj] = mfma_e4m3_16x16x128(fb[fs][jj], fa[fs][0]);
-                    fetch_a(Next{}, NSet{}, 0);
-#pragma unroll
-                    for (int i = 1; i < MI; ++i) {
-#pragma unroll
-                        for (int jj = 0; jj < NJ; ++jj) {
-                            const v4f nx = mfma_e4m3_16x16x128(fb[fs][jj], fa[fs][i]);
-                            acc[i - 1][jj] += part[jj] * fsc[fs][i - 1];
-                            part[jj] = nx;
-                        }
-                        fetch_a(Next{}, NSet{}, i);
-                    }
-#pragma unroll
-                    for (int jj = 0; jj < NJ; ++jj)
-                        acc[MI - 1][jj] += part[jj] * fsc[fs][MI - 1];
-                } else {
-#pragma unroll
-                    for (int i = 0; i < MI; ++i)
-                        fetch_a(Next{}, NSet{}, i);
-                }
-            };
-            using C0 = std::integral_constant<int, 0>;
-            using C1 = std::integral_constant<int, 1>;
-            for (int j0 = 0; j0 < nk; j0 += 6) {
-                pstep(std::integral_constant<int, 0>{}, C0{}, j0);
-                if (j0 + 1 < nk)
-                    pstep(std::integral_constant<int, 1 % S>{}, C1{}, j0 + 1);
-                if (j0 + 2 < nk)
-                    pstep(std::integral_constant<int, 2 % S>{}, C0{}, j0 + 2);
-                if (j0 + 3 < nk)
-                    pstep(std::integral_constant<int, 3 % S>{}, C1{}, j0 + 3);
-                if (j0 + 4 < nk)
-                    pstep(std::integral_constant<int, 4 % S>{}, C0{}, j0 + 4);
-                if (j0 + 5 < nk)
-                    pstep(std::integral_constant<int, 5 % S>{}, C1{}, j0 + 5);
-            }
-        } else if constexpr (!C::kPingPong) {
-            for (int kb0 = 0; kb0 < nk; kb0 += S) {
-                step(std::integral_constant<int, 0>{}, kb0);
-                if (kb0 + 1 < nk)
-                    step(std::integral_constant<int, 1>{}, kb0 + 1);
-                if (S > 2 && kb0 + 2 < nk)
-                    step(std::integral_constant<int, 2 % S>{}, kb0 + 2);
-                if (S > 3 && kb0 + 3 < nk)
-                    step(std::integral_constant<int, 3 % S>{}, kb0 + 3);
-            }
-        } else {
-            // Ping-pong schedule. Waves 0-3 and 4-7 form two groups with one
-            // wave of each on every SIMD. A K block is processed in two
-            // halves (sub-tile rows [0, MI/2) and [MI/2, MI)), and group 1
-            // runs half a block behind group 0, so in every barrier interval
-            // one group starts a block (LDS fragment reads) while the other
-            // finishes one (MFMAs and promotion), and the SIMD's matrix core
-            // and VALU are fed from both.
-            //   slot A(k): group 0 -> half 0 of k,   group 1 -> half 1 of k-1
-            //   slot B(k): group 0 -> half 1 of k,   group 1 -> half 0 of k
-            // DMA for block k+S-1 goes into stage (k-1)%S at the start of
-            // B(k), after both groups have left block k-1; block k+1 must
-            // have landed before the barrier that ends B(k).
-            const int grp = wave >> 2;
-            v8i bf[NJ];
-            auto half = [&](auto stage_c, auto part_c) {
-                constexpr int st = decltype(stage_c)::value;
-                constexpr int i0 = decltype(part_c)::value * (MI / 2), i1 = i0 + MI / 2;
-                const uint8_t *As = smem + st * C::kStageBytes;
-                const uint8_t *Bs = As + C::kOffB;
-                const float *sas = reinterpret_cast<const float *>(As + C::kOffSa);
-                const float sb = reinterpret_cast<const float *>(As + C::kOffSb)[wn0 >> 7];
-                auto frag = [&](const uint8_t *t, int lo, int hi, int k) {
-                    return join(*reinterpret_cast<const uint4 *>(t + lo + 2048 * k),
-                                *reinterpret_cast<const uint4 *>(t + hi + 2048 * k));
-                };
-                if (i0 == 0) {
-#pragma unroll
-                    for (int j = 0; j < NJ; ++j)
-                        bf[j] = frag(Bs, fb_lo, fb_hi, j);
-                }
-                v8i af = frag(As, fa_lo, fa_hi, i0);
-                float sc = sas[wm0 + 16 * i0 + l16] * sb;
-                v4f part[NJ];
-#pragma unroll
-                for (int j = 0; j < NJ; ++j)
-                    part[j] = mfma_e4m3_16x16x128(bf[j], af);
-#pragma unroll
-                for (int i = i0 + 1; i < i1; ++i) {
-                    const v8i afn = frag(As, fa_lo, fa_hi, i);
-                    const float scn = sas[wm0 + 16 * i + l16] * sb;
-#pragma unroll
-                    for (int j = 0; j < NJ; ++j) {
-                        const v4f nx = mfma_e4m3_16x16x128(bf[j], afn);
-                        acc[i - 1][j] += part[j] * sc;
-                        part[j] = nx;
-                    }
-                    sc = scn;
-                }
-#pragma unroll
-                for (int j = 0; j < NJ; ++j)
-                    acc[i1 - 1][j] += part[j] * sc;
-            };
-            using H0 = std::integral_constant<int, 0>;
-            using H1 = std::integral_constant<int, 1>;
-
-            // block 0 (and the prologue's later blocks) landed
-            if (S - 2 <= nk - 1)
-                wait_stage<SEGW, S - 2>(per_stage);
-            else
-                wait_vmcnt<0>();
-            wg_barrier();
-
-            auto block = [&](auto stage_c, int k) {
-                constexpr int st = decltype(stage_c)::value;
-                using Prev = std::integral_constant<int, (st + S - 1) % S>;
-                // slot A(k)
-                if (wave_active) {
-                    if (grp == 0)
-                        half(stage_c, H0{});
-                    else if (k >= 1)
-                        half(Prev{}, H1{});
-                }
-                wg_barrier();
-                // slot B(k)
-                if (k + S - 1 < nk)
-                    issue(k + S - 1, (st + S - 1) % S);
-                if (wave_active) {
-                    if (grp == 0)
-                        half(stage_c, H1{});
-                    else
-                        half(stage_c, H0{});
-                }
-                if (k + 1 < nk) {
-                    if (k + S - 1 < nk)
-                        wait_stage<SEGW, S - 2>(per_stage);
-                    else
-                        wait_vmcnt<0>();
-                }
-                wg_barrier();
-            };
-            for (int kb0 = 0; kb0 < nk; kb0 += S) {
-                block(std::integral_constant<int, 0>{}, kb0);
-                if (kb0 + 1 < nk)
-                    block(std::integral_constant<int, 1>{}, kb0 + 1);
-                if (S > 2 && kb0 + 2 < nk)
-                    block(std::integral_constant<int, 2 % S>{}, kb0 + 2);
-                if (S > 3 && kb0 + 3 < nk)
-                    block(std::integral_constant<int, 3 % S>{}, kb0 + 3);
-            }
-            // slot A(nk): group 1 finishes the last block
-            if (grp == 1 && wave_active) {
-                const int last = (nk - 1) % S;
-                if (last == 0)
-                    half(std::integral_constant<int, 0>{}, H1{});
-                else if (S > 1 && last == 1)
-                    half(std::integral_constant<int, 1 % S>{}, H1{});
-                else if (S > 2 && last == 2)
-                    half(std::integral_constant<int, 2 % S>{}, H1{});
-                else if (S > 3)
-                    half(std::integral_constant<int, 3 % S>{}, H1{});
-            }
-        }
+        for (int j = 0; j < NJ; ++j)
+            acc[MI - 1][j] += part[j] * part_sc;
 
         uint16_t *Dg = p.D + (int64_t)g * p.d_stride_g;
 #pragma unroll
