@@ -185,6 +185,15 @@ def load_traffic(kernel_name):
     return ent.get("bytes_per_launch")
 
 
+def workload_shape(kind, p):
+    """Shape keys of a workload for the JSON config."""
+    if kind == "dense":
+        return {"M": p.M, "N": p.N, "K": p.K}
+    if kind == "contiguous":
+        return {"M_total": p.M_total, "N": p.N, "K": p.K, "G": p.G}
+    return {"G": p.G, "M_max": p.M_max, "N": p.N, "K": p.K}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -242,8 +251,8 @@ def main():
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(head["ms_per_step"], 6),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": "fp8_e4m3 (fp32 accumulate, bf16 out)", "data": "synthetic",
-        "config": {"workload": args.workload, "M": p.M, "N": p.N, "K": p.K,
-                   "lhs_scale": "1x128", "rhs_scale": "128x128", "operand_copies": head["copies"]},
+        "config": dict(workload_shape(kind, p), workload=args.workload, lhs_scale="1x128",
+                       rhs_scale="128x128", operand_copies=head["copies"]),
         "tflops": round(head["tflops"], 3),
         "roofline": roof,
         "cpu_baseline": cpu,

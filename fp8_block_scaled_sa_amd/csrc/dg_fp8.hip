@@ -300,9 +300,15 @@ int dg_fp8_grouped_gemm_contiguous(const void *A, int64_t lda, const float *sA, 
     p.M = (int)M_total; p.N = (int)N; p.K = (int)K; p.G = (int)G;
     if (!offsets_fit(lda, ldb, sa_stride_m))
         return DG_ERR_UNSUPPORTED;
-    if (N % 256 == 0 && tile_override() != 2)
-        return launch_tiles<dgk::kContiguous, CfgWide>(p, 1, dev.cus, (hipStream_t)stream);
-    return launch_tiles<dgk::kContiguous, CfgNarrow>(p, 1, dev.cus, (hipStream_t)stream);
+    switch (tile_override()) {
+    case 2: return launch_tiles<dgk::kContiguous, CfgNarrow>(p, 1, dev.cus, (hipStream_t)stream);
+    case 3: return launch_tiles<dgk::kContiguous, CfgWide>(p, 1, dev.cus, (hipStream_t)stream);
+    case 4: return launch_tiles<dgk::kContiguous, CfgDense>(p, 1, dev.cus, (hipStream_t)stream);
+    default:
+        if (N % 256 == 0)
+            return launch_tiles<dgk::kContiguous, CfgBig>(p, 1, dev.cus, (hipStream_t)stream);
+        return launch_tiles<dgk::kContiguous, CfgDense>(p, 1, dev.cus, (hipStream_t)stream);
+    }
 }
 
 int dg_fp8_grouped_gemm_masked(const void *A, int64_t lda, int64_t a_stride_g, const float *sA, int64_t sa_stride_g,

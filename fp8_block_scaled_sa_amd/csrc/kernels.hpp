@@ -254,7 +254,9 @@ __global__ void __launch_bounds__(C::kThreads, 1) tile_kernel(Params p)
     constexpr int BM = C::kBM, BN = C::kBN, S = C::kStages;
     constexpr int MI = C::kMI, NJ = C::kNJ;
     constexpr int SEGW = C::kSegPerWave;
-    static_assert(L != kContiguous || BM <= 128, "contiguous tiles stay inside one 128-row block");
+    static_assert(L != kContiguous || BM <= 256, "contiguous tiles span at most two 128-row blocks");
+    static_assert(L != kContiguous || C::kWM <= 128, "a wave's rows lie in one 128-row block");
+    static_assert(L != kContiguous || BM == 256 || 128 % BM == 0, "contiguous tile rows");
 
     __shared__ __attribute__((aligned(1024))) uint8_t smem[C::kSmemBytes];
 
@@ -283,7 +285,8 @@ __global__ void __launch_bounds__(C::kThreads, 1) tile_kernel(Params p)
 
         int rows;        // valid rows of this tile (the rest re-read the last valid row)
         int limit = 0;   // masked: valid rows of the group
-        int expert = 0;  // group whose B/sB this tile uses
+        int npass = 1;   // contiguous: one K loop per expert met in the tile
+        int ex0 = 0, ex1 = 0;  // contiguous: expert of the tile's first / second 128-row block
         if (L == kDense) {
             rows = min(BM, p.M - m0);
         } else if (L == kMasked) {
@@ -291,22 +294,42 @@ __global__ void __launch_bounds__(C::kThreads, 1) tile_kernel(Params p)
             if (m0 >= limit)
                 continue;  // uniform over the workgroup
             rows = min(BM, limit - m0);
-            expert = g;
         } else {
-            // Expert of the aligned 128-row block: the largest valid id in it.
-            const int blk0 = m0 & ~127;
-            int e0 = p.ids[blk0 + lane], e1 = p.ids[blk0 + 64 + lane];
-            e0 = (e0 >= 0 && e0 < p.G) ? e0 : -1;
-            e1 = (e1 >= 0 && e1 < p.G) ? e1 : -1;
-            int e = max(e0, e1);
-            for (int o = 32; o > 0; o >>= 1)
-                e = max(e, __shfl_xor(e, o));
-            e = __builtin_amdgcn_readfirstlane(e);
-            if (e < 0)
+            // Expert of an aligned 128-row block: the largest valid id in it
+            // (-1 if it holds padding only or lies past M_total).
+            auto block_expert = [&](int blk0) {
+                if (blk0 >= p.M)
+                    return -1;
+                int e0 = p.ids[blk0 + lane], e1 = p.ids[blk0 + 64 + lane];
+                e0 = (e0 >= 0 && e0 < p.G) ? e0 : -1;
+                e1 = (e1 >= 0 && e1 < p.G) ? e1 : -1;
+                int e = max(e0, e1);
+                for (int o = 32; o > 0; o >>= 1)
+                    e = max(e, __shfl_xor(e, o));
+                return __builtin_amdgcn_readfirstlane(e);
+            };
+            ex0 = block_expert(m0 & ~127);
+            ex1 = BM > 128 ? block_expert(m0 + 128) : ex0;
+            if (ex0 < 0 && ex1 < 0)
                 continue;
-            expert = e;
+            // Blocks of two experts (a segment boundary) take two passes,
+            // each computing the half of its own expert; a padding-only half
+            // takes none.
+            if (ex0 != ex1 && ex0 >= 0 && ex1 >= 0)
+                npass = 2;
+            else if (ex0 < 0)
+                ex0 = ex1;
+            else
+                ex1 = ex0;
             rows = min(BM, p.M - m0);
         }
+
+        for (int pass = 0; pass < npass; ++pass) {
+        int expert = 0;  // group whose B/sB this pass uses
+        if (L == kMasked)
+            expert = g;
+        else if (L == kContiguous)
+            expert = pass == 0 ? ex0 : ex1;
 
         const uint8_t *Ab = p.A + (int64_t)g * p.a_stride_g + (int64_t)m0 * p.lda;
         const uint8_t *Bb = p.B + (int64_t)expert * p.b_stride_g + (int64_t)n0 * p.ldb;
@@ -371,7 +394,11 @@ __global__ void __launch_bounds__(C::kThreads, 1) tile_kernel(Params p)
             part[j] = v4f{0.f, 0.f, 0.f, 0.f};
         float part_sc = 0.f;   // scale of the row held in part
 
-        const bool wave_active = wm0 < rows;  // waves whose rows are all padding skip the math
+        // Waves whose rows are all padding, or (contiguous) belong to the other
+        // pass's expert, skip the math.
+        bool wave_active = wm0 < rows;
+        if (L == kContiguous && npass == 2)
+            wave_active = wave_active && ((wm0 < 128) == (pass == 0));
         auto compute = [&](auto stage_c) {
             constexpr int st = decltype(stage_c)::value;
             const uint8_t *As = smem + st * C::kStageBytes;
@@ -397,15 +424,14 @@ __global__ void __launch_bounds__(C::kThreads, 1) tile_kernel(Params p)
                 af[1] = frag(As, fa_lo, fa_hi, 1);
             __builtin_amdgcn_sched_barrier(0);
             const float sb = reinterpret_cast<const float *>(As + C::kOffSb)[wn0 >> 7];
-            float sa[MI];
-#pragma unroll
-            for (int i = 0; i < MI; ++i)
-                sa[i] = sas[wm0 + 16 * i + l16];
+            float sa = sas[wm0 + l16];  // sA of row i, read one row at a time
             __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
             for (int i = 0; i < MI; ++i) {
                 if (i >= 1 && i + 1 < MI)
                     af[(i + 1) & 1] = frag(As, fa_lo, fa_hi, i + 1);
+                if (i >= 1)
+                    sa = sas[wm0 + 16 * i + l16];
                 __builtin_amdgcn_sched_barrier(0);
                 // part holds row i-1 (the previous block's last row when i == 0)
                 const float sc = part_sc;
@@ -421,7 +447,7 @@ __global__ void __launch_bounds__(C::kThreads, 1) tile_kernel(Params p)
                     __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);  // four VALU
                 }
                 __builtin_amdgcn_sched_barrier(0);
-                part_sc = sa[i] * sb;
+                part_sc = sa * sb;
             }
         };
 
@@ -480,6 +506,7 @@ __global__ void __launch_bounds__(C::kThreads, 1) tile_kernel(Params p)
             for (int j = 0; j < NJ; ++j)
                 *reinterpret_cast<uint2 *>(drow + 16 * j) = pack_bf16x4(acc[i][j]);
         }
+        }  // pass
     }
 }
 
