@@ -55,8 +55,15 @@ def test_large_dense_sampled_parity(gpu_device, name):
     assert_close(got[ms, ns], ref, name)
 
 
-def test_small_contiguous_full_parity(gpu_device):
-    c = gen.make_contiguous(5, 700, 384, 640, 11, 12, 13)
+@pytest.mark.parametrize("N", [384, 512])   # 256x128 and 256x256 tiles
+def test_small_contiguous_full_parity(gpu_device, N):
+    # Segments of 1, 3, 1, 2 and 1 128-row blocks: three of the four 256-row
+    # tiles hold two experts (a pass per expert).
+    counts = [100, 300, 50, 129, 121]
+    tokens = np.repeat(np.arange(5), counts)
+    np.random.default_rng(14).shuffle(tokens)
+    c = gen.make_contiguous(5, len(tokens), N, 640, 11, 12, 13, expert_of_token=tokens)
+    assert c.M_total == 8 * 128
     ref = oracle.grouped_contiguous(c.a, c.sa_t.T, c.b, c.sb, c.ids,
                                     np.full((c.M_total, c.N), SENTINEL, np.uint16))
     got = run_contiguous(c)
@@ -80,8 +87,9 @@ def test_moe_contiguous_full_size(gpu_device):
     assert_close(got[rows, ns], ref, "moe contiguous")
 
 
-def test_small_masked_full_parity(gpu_device):
-    m = gen.make_masked(6, 200, 256, 512, 21, 22, 23, masked_m=np.array([0, 1, 200, 77, 128, 129]))
+@pytest.mark.parametrize("N", [256, 384])   # 256x256 and 256x128 tiles
+def test_small_masked_full_parity(gpu_device, N):
+    m = gen.make_masked(6, 200, N, 512, 21, 22, 23, masked_m=np.array([0, 1, 200, 77, 128, 129]))
     ref = oracle.grouped_masked(m.a, m.sa_t, m.b, m.sb, m.masked_m,
                                 np.full((m.G, m.M_max, m.N), SENTINEL, np.uint16))
     got = run_masked(m)
