@@ -96,6 +96,8 @@ int64_t last_scale_index(int64_t rows, int64_t nkb, int64_t s_row, int64_t s_kb)
 using CfgDense = dgk::TileCfg<256, 128, 4, 2, 3, 4>;
 using CfgDense4 = dgk::TileCfg<256, 128, 2, 2, 3, 4>;
 using CfgBig = dgk::TileCfg<256, 256, 2, 4, 2, 4>;  // 2 stages of 66 KB; N % 256 == 0
+// Masked layout: each group's B feeds one M tile, so B is streamed (non-temporal DMA).
+using CfgBigStreamB = dgk::TileCfg<256, 256, 2, 4, 2, 4, true>;
 using CfgWide = dgk::TileCfg<128, 256, 2, 2, 3, 8>;
 using CfgNarrow = dgk::TileCfg<128, 128, 2, 2, 4, 8>;
 
@@ -363,9 +365,11 @@ int dg_fp8_grouped_gemm_masked(const void *A, int64_t lda, int64_t a_stride_g, c
     case 1: return launch_tiles<dgk::kMasked, CfgDense4>(p, (int)G, dev.cus, (hipStream_t)stream);
     case 2: return launch_tiles<dgk::kMasked, CfgNarrow>(p, (int)G, dev.cus, (hipStream_t)stream);
     case 4: return launch_tiles<dgk::kMasked, CfgDense>(p, (int)G, dev.cus, (hipStream_t)stream);
+    case 12: return N % 256 == 0 ? launch_tiles<dgk::kMasked, CfgBig>(p, (int)G, dev.cus, (hipStream_t)stream)
+                                 : DG_ERR_UNSUPPORTED;
     default:
         if (N % 256 == 0)
-            return launch_tiles<dgk::kMasked, CfgBig>(p, (int)G, dev.cus, (hipStream_t)stream);
+            return launch_tiles<dgk::kMasked, CfgBigStreamB>(p, (int)G, dev.cus, (hipStream_t)stream);
         return launch_tiles<dgk::kMasked, CfgDense>(p, (int)G, dev.cus, (hipStream_t)stream);
     }
 }

@@ -147,6 +147,15 @@ __device__ __forceinline__ void dma_buf_b128(const v4i &rsrc, uint32_t voff, uin
                  : "memory", "m0");
 }
 
+// The same with the non-temporal hint, for data read once: it is not kept in
+// L2 at the expense of data that is re-read (another tile's operand rows).
+__device__ __forceinline__ void dma_buf_b128_nt(const v4i &rsrc, uint32_t voff, uint32_t soff, uint32_t m0)
+{
+    asm volatile("s_mov_b32 m0, %3\n\tbuffer_load_dwordx4 %0, %1, %2 offen nt lds" ::"v"(voff), "s"(rsrc),
+                 "s"(soff), "s"(m0)
+                 : "memory", "m0");
+}
+
 template <int N>
 __device__ __forceinline__ void wait_vmcnt()
 {
@@ -210,8 +219,11 @@ __device__ __forceinline__ void tile_coords(int t, int tiles_m, int tiles_n, int
 // columns must lie in one 128-wide sB block), WAVES_M x WAVES_N waves, each
 // owning a (BM/WAVES_M) x (BN/WAVES_N) block of 16x16 sub-tiles. STAGES LDS
 // buffers, each holding one K block of the A tile, the B tile and sA.
-template <int BM, int BN, int WAVES_M, int WAVES_N, int STAGES, int GROUP_M>
+template <int BM, int BN, int WAVES_M, int WAVES_N, int STAGES, int GROUP_M, bool STREAM_B = false>
 struct TileCfg {
+    // B rows are read once per launch (each group's B feeds a single M tile):
+    // load them non-temporally.
+    static constexpr bool kStreamB = STREAM_B;
     static constexpr int kBM = BM, kBN = BN, kStages = STAGES, kGroupM = GROUP_M;
     static constexpr int kWavesM = WAVES_M, kWavesN = WAVES_N;
     static constexpr int kWaves = WAVES_M * WAVES_N;
@@ -359,6 +371,9 @@ __global__ void __launch_bounds__(C::kThreads, 1) tile_kernel(Params p)
                 const int seg = q * C::kWaves + wave;
                 if (seg < C::kSegA)
                     dma_buf_b128(rsrc_a, voff_a + (uint32_t)(seg * 8 * p.lda), kb * 128, sbase + seg * 1024);
+                else if (C::kStreamB)
+                    dma_buf_b128_nt(rsrc_b, voff_b + (uint32_t)((seg - C::kSegA) * 8 * p.ldb), kb * 128,
+                                    sbase + seg * 1024);
                 else
                     dma_buf_b128(rsrc_b, voff_b + (uint32_t)((seg - C::kSegA) * 8 * p.ldb), kb * 128,
                                  sbase + seg * 1024);
