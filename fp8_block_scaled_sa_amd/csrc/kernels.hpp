@@ -237,6 +237,13 @@ struct TileCfg {
     static constexpr int kStageBytes = (kOffSb + 256 + 1023) / 1024 * 1024;  // + 64 sB slots; 1 KB aligned
     static constexpr int kNB = BN / 128;                    // sB blocks per tile
     static constexpr int kSmemBytes = STAGES * kStageBytes;
+    // With two stages every wave waits for all of its DMA before each
+    // barrier, so which waves issue the copies is free. The operand DMA then
+    // goes to the upper half of the waves: each SIMD's lower (older, issued
+    // first) wave starts its MFMAs right after the barrier, and the copies'
+    // issue stalls land on the wave that would otherwise wait for it there.
+    static constexpr bool kDmaUpper = STAGES == 2 && ((BM + BN) / 8) % (WAVES_M * WAVES_N / 2) == 0;
+    static constexpr int kDmaQ = kDmaUpper ? 2 * ((BM + BN) / 8) / (WAVES_M * WAVES_N) : ((BM + BN) / 8) / (WAVES_M * WAVES_N);
     static_assert(kWM % 16 == 0 && kWN % 16 == 0, "wave tile");
     static_assert((kSegA + kSegB) % kWaves == 0, "segments split evenly over waves");
     static_assert(BM % 64 == 0 && kSaLoads <= kWaves, "sA loads");
@@ -367,8 +374,11 @@ __global__ void __launch_bounds__(C::kThreads, 1) tile_kernel(Params p)
         auto issue = [&](int kb, int stage) {
             const uint32_t sbase = smem_base + stage * C::kStageBytes;
 #pragma unroll
-            for (int q = 0; q < SEGW; ++q) {
-                const int seg = q * C::kWaves + wave;
+            for (int q = 0; q < C::kDmaQ; ++q) {
+                // kDmaUpper: the upper half of the waves issues all segments.
+                const int seg = C::kDmaUpper ? q * (C::kWaves / 2) + (wave - C::kWaves / 2) : q * C::kWaves + wave;
+                if (C::kDmaUpper && wave < C::kWaves / 2)
+                    break;
                 if (seg < C::kSegA)
                     dma_buf_b128(rsrc_a, voff_a + (uint32_t)(seg * 8 * p.lda), kb * 128, sbase + seg * 1024);
                 else if (C::kStreamB)
