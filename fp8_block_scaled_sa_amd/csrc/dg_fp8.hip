@@ -136,26 +136,54 @@ bool offsets_fit(int64_t lda, int64_t ldb, int64_t sa_stride_m)
     return lda <= (1 << 22) && ldb <= (1 << 22) && sa_stride_m <= (1 << 20);
 }
 
+// LDS bytes of decode_dma_kernel<NB, MR, true>: LHS staging, B ring, sA.
+constexpr int decode_dma_lds(int nb, int mr)
+{
+    return dgk::kDecodeWaves * (nb * mr * 128 + 2 * 2048 + ((mr * nb + 63) / 64) * 64 * 4);
+}
+
+// decode_dma_kernel for NB K blocks per wave and MR staged LHS rows; false if
+// that instantiation does not fit the LDS.
+template <int MR>
+bool launch_decode_dma(const dgk::Params &p, int nb, bool full, hipStream_t stream)
+{
+    const dim3 g(p.N / 16), b(dgk::kDecodeThreads);
+    bool done = false;
+    auto one = [&](auto nb_c) {
+        constexpr int NB = decltype(nb_c)::value;
+        if constexpr (decode_dma_lds(NB, MR) <= 160 * 1024) {
+            if (nb != NB)
+                return;
+            if (full)
+                hipLaunchKernelGGL((dgk::decode_dma_kernel<NB, MR, true>), g, b, 0, stream, p);
+            else
+                hipLaunchKernelGGL((dgk::decode_dma_kernel<NB, MR, false>), g, b, 0, stream, p);
+            done = true;
+        }
+    };
+    one(std::integral_constant<int, 1>{});
+    one(std::integral_constant<int, 2>{});
+    one(std::integral_constant<int, 3>{});
+    one(std::integral_constant<int, 4>{});
+    one(std::integral_constant<int, 5>{});
+    one(std::integral_constant<int, 6>{});
+    one(std::integral_constant<int, 7>{});
+    one(std::integral_constant<int, 8>{});
+    return done;
+}
+
 int launch_decode(dgk::Params &p, hipStream_t stream)
 {
     const int grid = p.N / 16;
     hipError_t e;
     const int64_t nkb = p.K / 128;
-    if (p.M <= 8 && nkb % dgk::kDecodeWaves == 0 && nkb / dgk::kDecodeWaves <= 8 && tile_override() < 7 &&
-        (int64_t)(p.M - 1) * p.lda + p.K < ((int64_t)1 << 31) &&
-        ((int64_t)(p.M - 1) * p.sa_m + (nkb - 1) * p.sa_kb) * 4 < ((int64_t)1 << 31)) {
-        const dim3 g(grid), b(dgk::kDecodeThreads);
-        const bool full = tile_override() != 6;
-        switch (nkb / dgk::kDecodeWaves) {
-        case 1: if (full) hipLaunchKernelGGL((dgk::decode_dma_kernel<1, 8, true>), g, b, 0, stream, p); else hipLaunchKernelGGL((dgk::decode_dma_kernel<1, 8, false>), g, b, 0, stream, p); break;
-        case 2: if (full) hipLaunchKernelGGL((dgk::decode_dma_kernel<2, 8, true>), g, b, 0, stream, p); else hipLaunchKernelGGL((dgk::decode_dma_kernel<2, 8, false>), g, b, 0, stream, p); break;
-        case 3: if (full) hipLaunchKernelGGL((dgk::decode_dma_kernel<3, 8, true>), g, b, 0, stream, p); else hipLaunchKernelGGL((dgk::decode_dma_kernel<3, 8, false>), g, b, 0, stream, p); break;
-        case 4: if (full) hipLaunchKernelGGL((dgk::decode_dma_kernel<4, 8, true>), g, b, 0, stream, p); else hipLaunchKernelGGL((dgk::decode_dma_kernel<4, 8, false>), g, b, 0, stream, p); break;
-        case 5: if (full) hipLaunchKernelGGL((dgk::decode_dma_kernel<5, 8, true>), g, b, 0, stream, p); else hipLaunchKernelGGL((dgk::decode_dma_kernel<5, 8, false>), g, b, 0, stream, p); break;
-        case 6: if (full) hipLaunchKernelGGL((dgk::decode_dma_kernel<6, 8, true>), g, b, 0, stream, p); else hipLaunchKernelGGL((dgk::decode_dma_kernel<6, 8, false>), g, b, 0, stream, p); break;
-        case 7: if (full) hipLaunchKernelGGL((dgk::decode_dma_kernel<7, 8, true>), g, b, 0, stream, p); else hipLaunchKernelGGL((dgk::decode_dma_kernel<7, 8, false>), g, b, 0, stream, p); break;
-        default: if (full) hipLaunchKernelGGL((dgk::decode_dma_kernel<8, 8, true>), g, b, 0, stream, p); else hipLaunchKernelGGL((dgk::decode_dma_kernel<8, 8, false>), g, b, 0, stream, p); break;
-        }
+    const bool dma_ok = nkb % dgk::kDecodeWaves == 0 && nkb / dgk::kDecodeWaves <= 8 && tile_override() < 7 &&
+                        (int64_t)(p.M - 1) * p.lda + p.K < ((int64_t)1 << 31) &&
+                        ((int64_t)(p.M - 1) * p.sa_m + (nkb - 1) * p.sa_kb) * 4 < ((int64_t)1 << 31);
+    const int nb = (int)(nkb / dgk::kDecodeWaves);
+    const bool full = tile_override() != 6;
+    if (dma_ok && p.M <= 8 && launch_decode_dma<8>(p, nb, full, stream)) {
+    } else if (dma_ok && p.M <= 16 && launch_decode_dma<16>(p, nb, full, stream)) {
     } else if (p.M <= 16 && nkb % dgk::kDecodeWaves == 0 && nkb / dgk::kDecodeWaves <= 8 && tile_override() != 7 &&
         tile_override() != 8) {
         const dim3 g(grid), b(dgk::kDecodeThreads);

@@ -816,11 +816,13 @@ __global__ void __launch_bounds__(kDecodeThreads, 1) decode_dma_kernel(Params p)
     static_assert(MR == 8 || MR == 16, "LHS rows staged per block");
     constexpr int kBlk = MR * 128;                 // LDS bytes per K block of the LHS
     constexpr int kOps = NB * MR / 8;              // 1 KB DMA ops per wave for the LHS
-    static_assert(MR * NB <= 64, "one dword DMA op carries a wave's sA");
+    constexpr int kSaOps = (MR * NB + 63) / 64;    // dword DMA ops per wave for its sA
     __shared__ __attribute__((aligned(1024))) uint8_t a_lds[kDecodeWaves][NB * kBlk];
     __shared__ __attribute__((aligned(1024))) uint8_t b_ring[kDecodeWaves][BFULL ? 2 : 1][2048];
-    __shared__ float sa_lds[kDecodeWaves][64];
-    __shared__ v4f red[kDecodeWaves][64];
+    __shared__ float sa_lds[kDecodeWaves][kSaOps * 64];
+    // Each wave hands its partials to the reduction through its own LHS
+    // staging area, which it has finished reading by then.
+    static_assert(sizeof(v4f) * 64 <= NB * kBlk, "reduction slot");
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -841,10 +843,12 @@ __global__ void __launch_bounds__(kDecodeThreads, 1) decode_dma_kernel(Params p)
         const uint32_t voff = r < M ? (uint32_t)(r * p.lda + (kb0 + u) * 128 + ch * 16) : 0xffffffffu;
         dma_buf_b128(rsrc_a, voff, 0u, a_base + q * 1024);
     }
-    {   // sA for (row, block) = (lane % MR, lane / MR)
-        const int r = lane % MR, u = min(lane / MR, NB - 1);
+#pragma unroll
+    for (int o = 0; o < kSaOps; ++o) {  // sA for (row, block) = (i % MR, i / MR), i = 64 o + lane
+        const int i = 64 * o + lane;
+        const int r = i % MR, u = min(i / MR, NB - 1);
         const int rr = r < M ? r : 0;
-        dma_b32(p.sA, (uint32_t)((rr * p.sa_m + (int64_t)(kb0 + u) * p.sa_kb) * 4), lds_addr(&sa_lds[wave][0]));
+        dma_b32(p.sA, (uint32_t)((rr * p.sa_m + (int64_t)(kb0 + u) * p.sa_kb) * 4), lds_addr(&sa_lds[wave][64 * o]));
     }
     // 2. sB for the wave's blocks, one per lane.
     const float *sbp = p.sB + (int64_t)(n0 >> 7) * p.sb_nb + (int64_t)kb0 * p.sb_kb;
@@ -909,13 +913,13 @@ __global__ void __launch_bounds__(kDecodeThreads, 1) decode_dma_kernel(Params p)
         acc += part * (sa * sb);
     }
 
-    red[wave][lane] = acc;
+    reinterpret_cast<v4f *>(&a_lds[wave][0])[lane] = acc;
     __syncthreads();
     if (wave == 0) {
-        v4f v = red[0][lane];
+        v4f v = reinterpret_cast<const v4f *>(&a_lds[0][0])[lane];
 #pragma unroll
         for (int w = 1; w < kDecodeWaves; ++w)
-            v += red[w][lane];
+            v += reinterpret_cast<const v4f *>(&a_lds[w][0])[lane];
         if (arow)
             *reinterpret_cast<uint2 *>(p.D + (int64_t)l16 * p.ldd + n0 + 4 * lg) = pack_bf16x4(v);
     }
