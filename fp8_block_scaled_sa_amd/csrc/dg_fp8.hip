@@ -3,6 +3,8 @@
 // launch. No device memory is allocated and no stream is synchronised.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
+#include <map>
 #include <mutex>
 #include <stdlib.h>
 #include <stdint.h>
@@ -55,6 +57,45 @@ int current_device(DeviceInfo &out)
     return d.gfx950 ? DG_OK : DG_ERR_UNSUPPORTED;
 }
 
+// Split-K partial sums live in a device buffer per (device, stream), kept for
+// the life of the process and grown on demand. Calls on one stream run in
+// order, so they can share it; calls on different streams get their own.
+struct Workspace {
+    float *ptr = nullptr;
+    size_t bytes = 0;
+};
+std::map<std::pair<int, hipStream_t>, Workspace> g_workspaces;
+std::mutex g_workspaces_mu;
+
+// A buffer of at least `bytes` for `stream`, or nullptr (allocation failed).
+// Growing waits for the stream, whose queued kernels may still use the old one.
+float *stream_workspace(hipStream_t stream, size_t bytes)
+{
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess)
+        return nullptr;
+    std::lock_guard<std::mutex> lk(g_workspaces_mu);
+    Workspace &w = g_workspaces[{dev, stream}];
+    if (w.bytes >= bytes)
+        return w.ptr;
+    if (w.ptr) {
+        if (hipStreamSynchronize(stream) != hipSuccess)
+            return nullptr;
+        (void)hipFree(w.ptr);
+        w.ptr = nullptr;
+        w.bytes = 0;
+    }
+    const size_t want = (bytes + (1u << 20) - 1) & ~(size_t)((1u << 20) - 1);
+    void *ptr = nullptr;
+    if (hipMalloc(&ptr, want) != hipSuccess) {
+        (void)hipGetLastError();  // clear the sticky error; the caller falls back to no split
+        return nullptr;
+    }
+    w.ptr = (float *)ptr;
+    w.bytes = want;
+    return w.ptr;
+}
+
 bool aligned(const void *p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
 
 // [lo, hi) byte extent of a strided 2-D/3-D operand (all strides >= 0).
@@ -101,7 +142,12 @@ using CfgBigStreamB = dgk::TileCfg<256, 256, 2, 4, 2, 4, true>;
 using CfgWide = dgk::TileCfg<128, 256, 2, 2, 3, 8>;
 using CfgNarrow = dgk::TileCfg<128, 128, 2, 2, 4, 8>;
 
-// Optional override of the tile configuration, read once: DG_TILE=<index>.
+// Optional override of the kernel choice, read once: DG_TILE=<index>, for
+// measurements. 1, 2, 4: dense on 256x128 (4 waves), 128x128 or 256x128 tiles
+// without split-K; 6: decode with B loaded in operand layout; 7, 8, 9: older
+// decode kernels; 12: masked B loaded without the non-temporal hint; 13 / 14:
+// decode kernels up to M = 16 / 64; 15: split-K always on 256-wide tiles;
+// 16: no split-K; 2, 3, 4 also pick the contiguous layout's tile shape.
 int tile_override()
 {
     static int v = [] {
@@ -126,6 +172,36 @@ int launch_tiles(dgk::Params &p, int groups, int cus, hipStream_t stream)
         return DG_OK;
     const int grid = p.num_tiles < cus ? p.num_tiles : cus;  // persistent: one workgroup per CU
     hipLaunchKernelGGL((dgk::tile_kernel<L, C>), dim3(grid), dim3(C::kThreads), 0, stream, p);
+    hipError_t e = hipGetLastError();
+    return e == hipSuccess ? DG_OK : fail_hip(e);
+}
+
+// Dense GEMM on configuration C. When the tiles fill at most half of the CUs
+// (small M, or small M x N), each tile's K blocks are split over ks work items
+// (tiles * ks <= CUs, one round) that write fp32 partials; a second kernel
+// adds the slices in order and writes D.
+template <class C>
+int launch_dense(dgk::Params &p, int cus, hipStream_t stream)
+{
+    if (p.N % C::kBN != 0)
+        return DG_ERR_UNSUPPORTED;
+    const int64_t tiles = (int64_t)((p.M + C::kBM - 1) / C::kBM) * (p.N / C::kBN);
+    const int nk = p.K / 128;
+    int ks = 1;
+    if (tile_override() != 16 && tiles * 2 <= cus && nk >= 2)
+        ks = (int)std::min<int64_t>(std::min<int64_t>(nk, cus / tiles), 8);
+    if (ks > 1) {
+        p.ws = stream_workspace(stream, (size_t)ks * p.M * p.N * sizeof(float));
+        if (!p.ws)
+            ks = 1;
+    }
+    p.ksplit = ks;
+    int st = launch_tiles<dgk::kDense, C>(p, ks, cus, stream);
+    if (st != DG_OK || ks == 1)
+        return st;
+    const int64_t quads = (int64_t)p.M * (p.N / 4);
+    hipLaunchKernelGGL(dgk::splitk_reduce_kernel, dim3((unsigned)((quads + 255) / 256)), dim3(256), 0, stream,
+                       p.ws, ks, p.M, p.N, p.D, p.ldd);
     hipError_t e = hipGetLastError();
     return e == hipSuccess ? DG_OK : fail_hip(e);
 }
@@ -269,7 +345,11 @@ int dg_fp8_gemm_nt(const void *A, int64_t lda, const float *sA, int64_t sa_strid
     p.D = (uint16_t *)D; p.ldd = ldd;
     p.M = (int)M; p.N = (int)N; p.K = (int)K; p.G = 1;
     hipStream_t s = (hipStream_t)stream;
-    if (M <= 64 && (tile_override() < 0 || (tile_override() >= 7 && tile_override() <= 9)))
+    // M <= 24: the decode kernels (B streamed once per launch, LHS from L2).
+    // Larger M goes to the tile kernel, split over K when its tiles are few.
+    const int64_t decode_max_m = tile_override() == 13 ? 16 : tile_override() == 14 ? 64 : 24;
+    const bool forced_tiles = tile_override() == 1 || tile_override() == 2 || tile_override() == 4;
+    if (M <= decode_max_m && !forced_tiles)
         return launch_decode(p, s);
     if (!offsets_fit(lda, ldb, sa_stride_m))
         return DG_ERR_UNSUPPORTED;
@@ -278,10 +358,17 @@ int dg_fp8_gemm_nt(const void *A, int64_t lda, const float *sA, int64_t sa_strid
     case 1: return launch_tiles<dgk::kDense, CfgDense4>(p, 1, dev.cus, s);
     case 2: return launch_tiles<dgk::kDense, CfgNarrow>(p, 1, dev.cus, s);
     case 4: return launch_tiles<dgk::kDense, CfgDense>(p, 1, dev.cus, s);
-    default:
-        if (wide_n)
-            return launch_tiles<dgk::kDense, CfgBig>(p, 1, dev.cus, s);
-        return launch_tiles<dgk::kDense, CfgDense>(p, 1, dev.cus, s);
+    case 15: return wide_n ? launch_dense<CfgBig>(p, dev.cus, s) : launch_dense<CfgDense>(p, dev.cus, s);
+    default: {
+        // 256x256 tiles while they fill the CUs; below that, smaller tiles
+        // split over K (more work items per byte of partial sums).
+        const int64_t big_tiles = ((M + 255) / 256) * (N / 256);
+        if (wide_n && big_tiles * 2 > dev.cus)
+            return launch_dense<CfgBig>(p, dev.cus, s);
+        if (M <= 128)
+            return launch_dense<CfgNarrow>(p, dev.cus, s);
+        return launch_dense<CfgDense>(p, dev.cus, s);
+    }
     }
 }
 

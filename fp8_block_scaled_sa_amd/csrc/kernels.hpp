@@ -53,6 +53,11 @@ struct Params {
     int M;                    // dense M, contiguous M_total, masked M_max
     int N, K, G;
     int tiles_m, tiles_n, num_tiles;
+    // Dense split-K: each tile's K blocks are split over ksplit work items,
+    // which write fp32 partials to ws[ksplit][M][N]; splitk_reduce_kernel
+    // adds them in slice order. ksplit <= 1: no split, bf16 written directly.
+    int ksplit;
+    float *ws;
 };
 
 // One e4m3 x e4m3 -> fp32 MFMA over a 16x16x128 block, C = 0 + A.B.
@@ -285,7 +290,8 @@ __global__ void __launch_bounds__(C::kThreads, 1) tile_kernel(Params p)
     const int l16 = lane & 15, lg = lane >> 4;
     const int wm0 = (wave / C::kWavesN) * C::kWM;
     const int wn0 = (wave % C::kWavesN) * C::kWN;
-    const int nk = p.K >> 7;
+    const int nk_all = p.K >> 7;
+    const int ks = (L == kDense && p.ksplit > 1) ? p.ksplit : 1;
     const int tiles_per_group = p.tiles_m * p.tiles_n;
     const uint32_t smem_base = lds_addr(smem);
     const bool loads_sa = wave < C::kSaLoads;
@@ -294,11 +300,15 @@ __global__ void __launch_bounds__(C::kThreads, 1) tile_kernel(Params p)
 
     for (int t = xcd_local_id(blockIdx.x, gridDim.x); t < p.num_tiles; t += gridDim.x) {
         int g = 0, mt, nt;
+        // split-K: work item t is K slice t % ks of tile t / ks
+        const int slice = t % ks;
+        const int kb_lo = (int)((int64_t)slice * nk_all / ks);
+        const int nk = (int)((int64_t)(slice + 1) * nk_all / ks) - kb_lo;  // K blocks of this item
         if (L == kMasked) {
             g = t / tiles_per_group;
             tile_coords(t - g * tiles_per_group, p.tiles_m, p.tiles_n, C::kGroupM, mt, nt);
         } else {
-            tile_coords(t, p.tiles_m, p.tiles_n, C::kGroupM, mt, nt);
+            tile_coords(t / ks, p.tiles_m, p.tiles_n, C::kGroupM, mt, nt);
         }
         const int m0 = mt * BM, n0 = nt * BN;
 
@@ -350,10 +360,10 @@ __global__ void __launch_bounds__(C::kThreads, 1) tile_kernel(Params p)
         else if (L == kContiguous)
             expert = pass == 0 ? ex0 : ex1;
 
-        const uint8_t *Ab = p.A + (int64_t)g * p.a_stride_g + (int64_t)m0 * p.lda;
-        const uint8_t *Bb = p.B + (int64_t)expert * p.b_stride_g + (int64_t)n0 * p.ldb;
-        const float *sAb = p.sA + (int64_t)g * p.sa_g + (int64_t)m0 * p.sa_m;
-        const float *sBb = p.sB + (int64_t)expert * p.sb_g + (int64_t)(n0 >> 7) * p.sb_nb;
+        const uint8_t *Ab = p.A + (int64_t)g * p.a_stride_g + (int64_t)m0 * p.lda + (int64_t)kb_lo * 128;
+        const uint8_t *Bb = p.B + (int64_t)expert * p.b_stride_g + (int64_t)n0 * p.ldb + (int64_t)kb_lo * 128;
+        const float *sAb = p.sA + (int64_t)g * p.sa_g + (int64_t)m0 * p.sa_m + (int64_t)kb_lo * p.sa_kb;
+        const float *sBb = p.sB + (int64_t)expert * p.sb_g + (int64_t)(n0 >> 7) * p.sb_nb + (int64_t)kb_lo * p.sb_kb;
 
         // DMA of one K block. Segment s covers tile rows 8s..8s+7 (A rows
         // first, then B rows); lane i fills LDS bytes 16 i of it: row
@@ -526,6 +536,13 @@ __global__ void __launch_bounds__(C::kThreads, 1) tile_kernel(Params p)
                 ok = m < p.M && p.ids[m] == expert;
             if (!ok)
                 continue;
+            if (ks > 1) {
+                float *wrow = p.ws + ((int64_t)slice * p.M + m) * p.N + n0 + wn0 + 4 * lg;
+#pragma unroll
+                for (int j = 0; j < NJ; ++j)
+                    *reinterpret_cast<v4f *>(wrow + 16 * j) = acc[i][j];
+                continue;
+            }
             uint16_t *drow = Dg + (int64_t)m * p.ldd + n0 + wn0 + 4 * lg;
 #pragma unroll
             for (int j = 0; j < NJ; ++j)
@@ -533,6 +550,23 @@ __global__ void __launch_bounds__(C::kThreads, 1) tile_kernel(Params p)
         }
         }  // pass
     }
+}
+
+// Second half of a dense split-K GEMM: D = bf16(sum over slices of ws[slice]),
+// slices added in order 0, 1, ... so the result does not depend on which work
+// item finished first. One thread per 4 consecutive outputs of a row.
+__global__ void __launch_bounds__(256) splitk_reduce_kernel(const float *ws, int ksplit, int M, int N,
+                                                            uint16_t *D, int64_t ldd)
+{
+    const int nq = N >> 2;
+    const int64_t q = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (q >= (int64_t)M * nq)
+        return;
+    const int m = (int)(q / nq), c = (int)(q - (int64_t)m * nq) * 4;
+    v4f s = *reinterpret_cast<const v4f *>(ws + (int64_t)m * N + c);
+    for (int k = 1; k < ksplit; ++k)
+        s += *reinterpret_cast<const v4f *>(ws + ((int64_t)k * M + m) * N + c);
+    *reinterpret_cast<uint2 *>(D + (int64_t)m * ldd + c) = pack_bf16x4(s);
 }
 
 // ---------------------------------------------------------------------------

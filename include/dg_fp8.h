@@ -21,10 +21,12 @@
  * "NT": A is [M, K] and B is [N, K], both with K contiguous, D = A . B^T.
  *
  * Conventions shared by every entry point
- *   - All pointers are DEVICE pointers owned by the caller. The library never
- *     allocates, frees, keeps a pointer past return, or synchronises.
+ *   - All pointers are DEVICE pointers owned by the caller; the library never
+ *     keeps one past return.
  *   - `stream` is a hipStream_t (NULL = the legacy default stream). The call
- *     validates its arguments on the host, enqueues one kernel and returns.
+ *     validates its arguments on the host, enqueues its kernels and returns.
+ *     It allocates nothing and does not synchronise, with one exception in
+ *     dg_fp8_gemm_nt (see there).
  *   - Strides are in elements. e4m3 is one byte, so A/B strides are also byte
  *     strides; D strides count bf16 elements. Scale tables are addressed
  *     logically through explicit strides: sA[m, kb] = sA[m*sa_stride_m +
@@ -37,7 +39,8 @@
  *   - Shapes: K > 0 and K % 128 == 0; N % 128 == 0; M arbitrary (>= 0).
  *   - D must not overlap A, B, sA, sB or the routing arrays.
  *   - Results are deterministic: no atomics, a fixed reduction order.
- *   - Thread-safe; the only global state is a per-device property cache.
+ *   - Thread-safe; the global state is a per-device property cache and the
+ *     split-K workspaces of dg_fp8_gemm_nt.
  *
  * Errors: every error is detected on the host before anything is enqueued,
  * and D is left untouched. DG_ERR_HIP reports a failed launch; the HIP error
@@ -82,6 +85,17 @@ int dg_last_hip_error(void);
  *   D  [M, N] bf16, row stride ldd (written)
  * Operation as in the header comment (lpnh.cn §2.3; hotdry.top, fine-grained
  * scaling core design).
+ *
+ * Split-K: when 24 < M and the output tiles would fill at most half of the
+ * GPU's CUs (e.g. M up to ~2000 at N = 4096), each tile's K blocks are split
+ * over up to 8 work items that write fp32 partial sums to a device workspace,
+ * and a second kernel adds them in a fixed order. The workspace (slices x M x
+ * N x 4 bytes) belongs to the library: one per (device, stream), allocated
+ * with hipMalloc on the first such call on that stream and regrown (after
+ * hipStreamSynchronize on that stream) when a call needs more. Such a call is
+ * therefore not capture-safe until the stream's workspace is large enough.
+ * Concurrent calls on different streams use different workspaces. If the
+ * allocation fails the call runs without the split.
  */
 int dg_fp8_gemm_nt(const void *A, int64_t lda,
                    const float *sA, int64_t sa_stride_m, int64_t sa_stride_kb,

@@ -30,6 +30,14 @@ def test_dense_full_parity(gpu_device, M, N, K):
     assert_close(got, ref, "dense %dx%dx%d" % (M, N, K))
 
 
+@pytest.mark.parametrize("M", [40, 96, 256])   # split over K: 128x128 / 256x128 tiles + reduction
+def test_medium_m_full_parity(gpu_device, M):
+    p = gen.make_dense(M, 4096, 7168, 3000 + M, 4000 + M)
+    ref = oracle.gemm_nt(p.a, p.sa_t.T, p.b, p.sb)
+    got = run_dense(p.a, p.sa_t.T, p.b, p.sb)
+    assert_close(got, ref, "dense %dx4096x7168" % M)
+
+
 def test_decode_full_parity(gpu_device):
     p = gen.make_config("decode_8x4096x7168")
     ref = oracle.gemm_nt(p.a, p.sa_t.T, p.b, p.sb)
