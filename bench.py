@@ -139,6 +139,9 @@ def time_workload(name, steps, warmup, rotate=True):
     graph = torch.cuda.CUDAGraph()
     cap = torch.cuda.Stream()
     cap.wait_stream(cur)
+    with torch.cuda.stream(cap):    # one eager launch on the capture stream sets up its split-K workspace
+        run(0)
+    cap.synchronize()
     with torch.cuda.graph(graph, stream=cap):
         for i in range(steps):
             run(warmup + i)

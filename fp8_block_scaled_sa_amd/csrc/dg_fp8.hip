@@ -67,7 +67,9 @@ struct Workspace {
 std::map<std::pair<int, hipStream_t>, Workspace> g_workspaces;
 std::mutex g_workspaces_mu;
 
-// A buffer of at least `bytes` for `stream`, or nullptr (allocation failed).
+// A buffer of at least `bytes` for `stream`, or nullptr (allocation failed,
+// or the stream is being captured into a graph and has no large-enough
+// buffer yet: nothing is allocated or synchronised during a capture).
 // Growing waits for the stream, whose queued kernels may still use the old one.
 float *stream_workspace(hipStream_t stream, size_t bytes)
 {
@@ -78,6 +80,9 @@ float *stream_workspace(hipStream_t stream, size_t bytes)
     Workspace &w = g_workspaces[{dev, stream}];
     if (w.bytes >= bytes)
         return w.ptr;
+    hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+    if (hipStreamIsCapturing(stream, &cs) != hipSuccess || cs != hipStreamCaptureStatusNone)
+        return nullptr;
     if (w.ptr) {
         if (hipStreamSynchronize(stream) != hipSuccess)
             return nullptr;
@@ -345,9 +350,11 @@ int dg_fp8_gemm_nt(const void *A, int64_t lda, const float *sA, int64_t sa_strid
     p.D = (uint16_t *)D; p.ldd = ldd;
     p.M = (int)M; p.N = (int)N; p.K = (int)K; p.G = 1;
     hipStream_t s = (hipStream_t)stream;
-    // M <= 24: the decode kernels (B streamed once per launch, LHS from L2).
-    // Larger M goes to the tile kernel, split over K when its tiles are few.
-    const int64_t decode_max_m = tile_override() == 13 ? 16 : tile_override() == 14 ? 64 : 24;
+    // Small M: the decode kernels (B streamed once per launch, LHS from L2),
+    // up to M = 24, or M = 64 when K is short (< 16 blocks: a split-K launch
+    // pair costs more than it saves). Larger M goes to the tile kernel, split
+    // over K when its tiles are few.
+    const int64_t decode_max_m = tile_override() == 13 ? 16 : tile_override() == 14 ? 64 : (nkb < 16 ? 64 : 24);
     const bool forced_tiles = tile_override() == 1 || tile_override() == 2 || tile_override() == 4;
     if (M <= decode_max_m && !forced_tiles)
         return launch_decode(p, s);

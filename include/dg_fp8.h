@@ -86,14 +86,16 @@ int dg_last_hip_error(void);
  * Operation as in the header comment (lpnh.cn §2.3; hotdry.top, fine-grained
  * scaling core design).
  *
- * Split-K: when 24 < M and the output tiles would fill at most half of the
+ * Split-K: when 24 < M (64 < M for K < 2048) and the output tiles would fill at most half of the
  * GPU's CUs (e.g. M up to ~2000 at N = 4096), each tile's K blocks are split
  * over up to 8 work items that write fp32 partial sums to a device workspace,
  * and a second kernel adds them in a fixed order. The workspace (slices x M x
  * N x 4 bytes) belongs to the library: one per (device, stream), allocated
  * with hipMalloc on the first such call on that stream and regrown (after
- * hipStreamSynchronize on that stream) when a call needs more. Such a call is
- * therefore not capture-safe until the stream's workspace is large enough.
+ * hipStreamSynchronize on that stream) when a call needs more. While the
+ * stream is being captured into a graph nothing is allocated: a call whose
+ * stream has no large-enough workspace yet runs without the split (so one
+ * eager call on the capture stream beforehand puts the split in the graph).
  * Concurrent calls on different streams use different workspaces. If the
  * allocation fails the call runs without the split.
  */

@@ -214,3 +214,46 @@ def test_empty_problems(gpu_device):
                            torch.zeros((128, 256), dtype=torch.uint8, device="cuda"),
                            torch.zeros((1, 2), device="cuda"))
     assert d.shape == (0, 128)
+
+
+def test_split_k_in_graph_capture(gpu_device):
+    # M=96, N=512 gives 4 tiles of 128x128, so the K blocks are split over
+    # work items and reduced by a second kernel. A capture on a stream that
+    # already ran the split replays bit-identically to the eager result (the
+    # slices are added in a fixed order); a capture on a fresh stream runs
+    # unsplit (nothing is allocated during a capture) and stays within
+    # tolerance of the oracle.
+    p = gen.make_dense(96, 512, 1024, 61, 62)
+    ref = oracle.gemm_nt(p.a, p.sa_t.T, p.b, p.sb)
+    a, sa, b, sb = dev(p.a), dev(p.sa_t).t(), dev(p.b), dev(p.sb)
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    d = sentinel_bf16((96, 512))
+    with torch.cuda.stream(s):
+        ops.dg_fp8_gemm_nt(a, sa, b, sb, d=d)
+    s.synchronize()
+    eager = bits(d)
+    assert_close(eager, ref, "split-K eager")
+    g = torch.cuda.CUDAGraph()
+    d2 = sentinel_bf16((96, 512))
+    with torch.cuda.graph(g, stream=s):
+        ops.dg_fp8_gemm_nt(a, sa, b, sb, d=d2)
+    for r in range(3):
+        d2.fill_(0)
+        torch.cuda.synchronize()
+        with torch.cuda.stream(s):
+            g.replay()
+        s.synchronize()
+        assert np.array_equal(bits(d2), eager), "replay %d" % r
+        ops.dg_fp8_gemm_nt(a, sa, b, sb, d=d)   # eager work between replays
+        torch.cuda.synchronize()
+    fresh = torch.cuda.Stream()
+    fresh.wait_stream(torch.cuda.current_stream())
+    g2 = torch.cuda.CUDAGraph()
+    d3 = sentinel_bf16((96, 512))
+    with torch.cuda.graph(g2, stream=fresh):
+        ops.dg_fp8_gemm_nt(a, sa, b, sb, d=d3)
+    with torch.cuda.stream(fresh):
+        g2.replay()
+    fresh.synchronize()
+    assert_close(bits(d3), ref, "unsplit in capture")
