@@ -151,7 +151,8 @@ using CfgNarrow = dgk::TileCfg<128, 128, 2, 2, 4, 8>;
 // measurements. 1, 2, 4: dense on 256x128 (4 waves), 128x128 or 256x128 tiles
 // without split-K; 6: decode with B loaded in operand layout; 7, 8, 9: older
 // decode kernels; 12: masked B loaded without the non-temporal hint; 13 / 14:
-// decode kernels up to M = 16 / 64; 15: split-K always on 256-wide tiles;
+// decode kernels up to M = 16 / all older decode kernels up to 64; 15:
+// split-K always on 256-wide tiles;
 // 16: no split-K; 2, 3, 4 also pick the contiguous layout's tile shape.
 int tile_override()
 {
@@ -225,20 +226,20 @@ constexpr int decode_dma_lds(int nb, int mr)
 
 // decode_dma_kernel for NB K blocks per wave and MR staged LHS rows; false if
 // that instantiation does not fit the LDS.
-template <int MR>
+template <int MR, int MP = 1>
 bool launch_decode_dma(const dgk::Params &p, int nb, bool full, hipStream_t stream)
 {
     const dim3 g(p.N / 16), b(dgk::kDecodeThreads);
     bool done = false;
     auto one = [&](auto nb_c) {
         constexpr int NB = decltype(nb_c)::value;
-        if constexpr (decode_dma_lds(NB, MR) <= 160 * 1024) {
+        if constexpr (decode_dma_lds(NB, MR) <= 160 * 1024 && MP * 1024 <= NB * MR * 128) {
             if (nb != NB)
                 return;
             if (full)
-                hipLaunchKernelGGL((dgk::decode_dma_kernel<NB, MR, true>), g, b, 0, stream, p);
+                hipLaunchKernelGGL((dgk::decode_dma_kernel<NB, MR, true, MP>), g, b, 0, stream, p);
             else
-                hipLaunchKernelGGL((dgk::decode_dma_kernel<NB, MR, false>), g, b, 0, stream, p);
+                hipLaunchKernelGGL((dgk::decode_dma_kernel<NB, MR, false, MP>), g, b, 0, stream, p);
             done = true;
         }
     };
@@ -253,18 +254,30 @@ bool launch_decode_dma(const dgk::Params &p, int nb, bool full, hipStream_t stre
     return done;
 }
 
-int launch_decode(dgk::Params &p, hipStream_t stream)
+// Returned by launch_decode when it leaves the problem to the tile kernel.
+constexpr int kDecodeDeclined = -1;
+
+// Small-M kernels. The LHS-staging kernel (up to 4 passes of 16 rows) is
+// tried first; when its LDS does not fit the shape, the older decode kernels
+// run if `fallback` (M <= 24 or short K), else kDecodeDeclined.
+int launch_decode(dgk::Params &p, hipStream_t stream, bool fallback)
 {
     const int grid = p.N / 16;
     hipError_t e;
     const int64_t nkb = p.K / 128;
-    const bool dma_ok = nkb % dgk::kDecodeWaves == 0 && nkb / dgk::kDecodeWaves <= 8 && tile_override() < 7 &&
+    const bool dma_ok = nkb % dgk::kDecodeWaves == 0 && nkb / dgk::kDecodeWaves <= 8 &&
+                        (tile_override() < 7 || tile_override() > 9) &&
                         (int64_t)(p.M - 1) * p.lda + p.K < ((int64_t)1 << 31) &&
                         ((int64_t)(p.M - 1) * p.sa_m + (nkb - 1) * p.sa_kb) * 4 < ((int64_t)1 << 31);
     const int nb = (int)(nkb / dgk::kDecodeWaves);
     const bool full = tile_override() != 6;
     if (dma_ok && p.M <= 8 && launch_decode_dma<8>(p, nb, full, stream)) {
     } else if (dma_ok && p.M <= 16 && launch_decode_dma<16>(p, nb, full, stream)) {
+    } else if (dma_ok && p.M <= 32 && launch_decode_dma<16, 2>(p, nb, full, stream)) {
+    } else if (dma_ok && p.M <= 48 && launch_decode_dma<16, 3>(p, nb, full, stream)) {
+    } else if (dma_ok && p.M <= 64 && launch_decode_dma<16, 4>(p, nb, full, stream)) {
+    } else if (!fallback) {
+        return kDecodeDeclined;
     } else if (p.M <= 16 && nkb % dgk::kDecodeWaves == 0 && nkb / dgk::kDecodeWaves <= 8 && tile_override() != 7 &&
         tile_override() != 8) {
         const dim3 g(grid), b(dgk::kDecodeThreads);
@@ -350,14 +363,18 @@ int dg_fp8_gemm_nt(const void *A, int64_t lda, const float *sA, int64_t sa_strid
     p.D = (uint16_t *)D; p.ldd = ldd;
     p.M = (int)M; p.N = (int)N; p.K = (int)K; p.G = 1;
     hipStream_t s = (hipStream_t)stream;
-    // Small M: the decode kernels (B streamed once per launch, LHS from L2),
-    // up to M = 24, or M = 64 when K is short (< 16 blocks: a split-K launch
-    // pair costs more than it saves). Larger M goes to the tile kernel, split
-    // over K when its tiles are few.
-    const int64_t decode_max_m = tile_override() == 13 ? 16 : tile_override() == 14 ? 64 : (nkb < 16 ? 64 : 24);
+    // M <= 64: the decode kernels (B streamed once per launch, the LHS staged
+    // per wave 16 rows at a time). Where their LDS staging does not fit the
+    // shape, the older decode kernels keep M <= 24 and short K (< 16 blocks:
+    // a split-K launch pair costs more than it saves); the rest, and all
+    // larger M, go to the tile kernel, split over K when its tiles are few.
     const bool forced_tiles = tile_override() == 1 || tile_override() == 2 || tile_override() == 4;
-    if (M <= decode_max_m && !forced_tiles)
-        return launch_decode(p, s);
+    const int64_t decode_max_m = tile_override() == 13 ? 16 : 64;
+    if (M <= decode_max_m && !forced_tiles) {
+        st = launch_decode(p, s, M <= 24 || nkb < 16 || tile_override() == 14);
+        if (st != kDecodeDeclined)
+            return st;
+    }
     if (!offsets_fit(lda, ldb, sa_stride_m))
         return DG_ERR_UNSUPPORTED;
     const bool wide_n = N % 256 == 0;

@@ -844,10 +844,15 @@ __global__ void __launch_bounds__(kDecodeThreads, 1) decode_static_kernel(Params
 // sB and issues its B blocks (the HBM stream) straight into MFMA operand
 // registers. No barrier precedes the math: a wave only reads its own LDS
 // region, and each block's MFMA waits for that block's B alone.
-template <int NB, int MR, bool BFULL>
+template <int NB, int MR, bool BFULL, int MP = 1>
 __global__ void __launch_bounds__(kDecodeThreads, 1) decode_dma_kernel(Params p)
 {
+    // MP passes of MR = 16 LHS rows each (M <= 16 MP): B is loaded and put
+    // in operand layout once; each later pass restages the next 16 rows of
+    // the wave's LHS blocks in the same LDS area.
     static_assert(MR == 8 || MR == 16, "LHS rows staged per block");
+    static_assert(MP == 1 || MR == 16, "multi-pass stages 16 rows per pass");
+    static_assert(MP >= 1 && MP <= kDecodeWaves, "one reducing wave per pass");
     constexpr int kBlk = MR * 128;                 // LDS bytes per K block of the LHS
     constexpr int kOps = NB * MR / 8;              // 1 KB DMA ops per wave for the LHS
     constexpr int kSaOps = (MR * NB + 63) / 64;    // dword DMA ops per wave for its sA
@@ -856,7 +861,7 @@ __global__ void __launch_bounds__(kDecodeThreads, 1) decode_dma_kernel(Params p)
     __shared__ float sa_lds[kDecodeWaves][kSaOps * 64];
     // Each wave hands its partials to the reduction through its own LHS
     // staging area, which it has finished reading by then.
-    static_assert(sizeof(v4f) * 64 <= NB * kBlk, "reduction slot");
+    static_assert(sizeof(v4f) * 64 * MP <= NB * kBlk, "reduction slot");
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -866,24 +871,30 @@ __global__ void __launch_bounds__(kDecodeThreads, 1) decode_dma_kernel(Params p)
     const int kb0 = wave * NB;
     const int M = p.M;
 
-    // 1. LHS: op q covers rows 8(q%(MR/8))..+7 of block q/(MR/8); lane i takes
-    // row +i/8, physical chunk i%8 = logical chunk (i%8) ^ swz(row).
+    // 1. LHS rows [16 pass, 16 pass + MR): op q covers rows 8(q%(MR/8))..+7 of
+    // block q/(MR/8); lane i takes row +i/8, physical chunk i%8 = logical
+    // chunk (i%8) ^ swz(row). Rows >= M read as zeros (offset past the buffer).
     const uint32_t a_base = lds_addr(&a_lds[wave][0]);
     const v4i rsrc_a = buffer_rsrc(p.A, (uint32_t)((int64_t)(M - 1) * p.lda + p.K));
+    auto stage_lhs = [&](int pass) {
 #pragma unroll
-    for (int q = 0; q < kOps; ++q) {
-        const int u = q / (MR / 8), r = (q % (MR / 8)) * 8 + (lane >> 3);
-        const int ch = (lane & 7) ^ swz(r);
-        const uint32_t voff = r < M ? (uint32_t)(r * p.lda + (kb0 + u) * 128 + ch * 16) : 0xffffffffu;
-        dma_buf_b128(rsrc_a, voff, 0u, a_base + q * 1024);
-    }
+        for (int q = 0; q < kOps; ++q) {
+            const int u = q / (MR / 8), r = (q % (MR / 8)) * 8 + (lane >> 3);
+            const int ch = (lane & 7) ^ swz(r);
+            const int row = MR * pass + r;
+            const uint32_t voff = row < M ? (uint32_t)(row * p.lda + (kb0 + u) * 128 + ch * 16) : 0xffffffffu;
+            dma_buf_b128(rsrc_a, voff, 0u, a_base + q * 1024);
+        }
 #pragma unroll
-    for (int o = 0; o < kSaOps; ++o) {  // sA for (row, block) = (i % MR, i / MR), i = 64 o + lane
-        const int i = 64 * o + lane;
-        const int r = i % MR, u = min(i / MR, NB - 1);
-        const int rr = r < M ? r : 0;
-        dma_b32(p.sA, (uint32_t)((rr * p.sa_m + (int64_t)(kb0 + u) * p.sa_kb) * 4), lds_addr(&sa_lds[wave][64 * o]));
-    }
+        for (int o = 0; o < kSaOps; ++o) {  // sA for (row, block) = (i % MR, i / MR), i = 64 o + lane
+            const int i = 64 * o + lane;
+            const int r = MR * pass + i % MR, u = min(i / MR, NB - 1);
+            const int rr = r < M ? r : 0;
+            dma_b32(p.sA, (uint32_t)((rr * p.sa_m + (int64_t)(kb0 + u) * p.sa_kb) * 4),
+                    lds_addr(&sa_lds[wave][64 * o]));
+        }
+    };
+    stage_lhs(0);
     // 2. sB for the wave's blocks, one per lane.
     const float *sbp = p.sB + (int64_t)(n0 >> 7) * p.sb_nb + (int64_t)kb0 * p.sb_kb;
     const float sbv = sbp[(int64_t)min(lane, NB - 1) * p.sb_kb];
@@ -917,45 +928,65 @@ __global__ void __launch_bounds__(kDecodeThreads, 1) decode_dma_kernel(Params p)
     // 1 + 2 NB loads are outstanding.
     wait_vmcnt<1 + 2 * NB>();
 
-    v4f acc = {0.f, 0.f, 0.f, 0.f};
-    const bool arow = l16 < M;
+    v4f acc[MP];
     const int fsw = swz(l16);
     const int fsw_a = swz(l16 & 7);
 #pragma unroll
-    for (int u = 0; u < NB; ++u) {
-        if constexpr (BFULL) {
-            uint8_t *slot = &b_ring[wave][u & 1][0];
+    for (int pass = 0; pass < MP; ++pass) {
+        if (pass > 0) {
+            // This wave's reads of the previous pass's LHS have returned (they
+            // fed its MFMAs); restage its area and wait for the copies only
+            // (every B load was consumed in pass 0).
+            asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+            stage_lhs(pass);
+            wait_vmcnt<0>();
+        }
+        acc[pass] = v4f{0.f, 0.f, 0.f, 0.f};
+        const bool arow = MR * pass + l16 < M;
 #pragma unroll
-            for (int j = 0; j < 2; ++j) {
-                const int r = 8 * j + (lane >> 3);
-                *reinterpret_cast<v4u *>(slot + r * 128 + (((lane & 7) ^ swz(r)) << 4)) = bl[u][j];
+        for (int u = 0; u < NB; ++u) {
+            if constexpr (BFULL) {
+                if (pass == 0) {
+                    uint8_t *slot = &b_ring[wave][u & 1][0];
+#pragma unroll
+                    for (int j = 0; j < 2; ++j) {
+                        const int r = 8 * j + (lane >> 3);
+                        *reinterpret_cast<v4u *>(slot + r * 128 + (((lane & 7) ^ swz(r)) << 4)) = bl[u][j];
+                    }
+                    const uint8_t *t = slot + l16 * 128;
+                    bf[u] = join(*reinterpret_cast<const uint4 *>(t + ((lg ^ fsw) << 4)),
+                                 *reinterpret_cast<const uint4 *>(t + (((lg + 4) ^ fsw) << 4)));
+                }
             }
-            const uint8_t *t = slot + l16 * 128;
-            bf[u] = join(*reinterpret_cast<const uint4 *>(t + ((lg ^ fsw) << 4)),
-                         *reinterpret_cast<const uint4 *>(t + (((lg + 4) ^ fsw) << 4)));
+            v8i af = v8i{0, 0, 0, 0, 0, 0, 0, 0};
+            float sa = 0.f;
+            if (arow) {
+                const uint8_t *t = &a_lds[wave][u * kBlk + l16 * 128];
+                af = join(*reinterpret_cast<const uint4 *>(t + ((lg ^ fsw_a) << 4)),
+                          *reinterpret_cast<const uint4 *>(t + (((lg + 4) ^ fsw_a) << 4)));
+                sa = sa_lds[wave][u * MR + l16];
+            }
+            const float sb = __shfl(sbv, u);
+            const v4f part = mfma_e4m3_16x16x128(bf[u], af);
+            acc[pass] += part * (sa * sb);
         }
-        v8i af = v8i{0, 0, 0, 0, 0, 0, 0, 0};
-        float sa = 0.f;
-        if (arow) {
-            const uint8_t *t = &a_lds[wave][u * kBlk + l16 * 128];
-            af = join(*reinterpret_cast<const uint4 *>(t + ((lg ^ fsw_a) << 4)),
-                      *reinterpret_cast<const uint4 *>(t + (((lg + 4) ^ fsw_a) << 4)));
-            sa = sa_lds[wave][u * MR + l16];
-        }
-        const float sb = __shfl(sbv, u);
-        const v4f part = mfma_e4m3_16x16x128(bf[u], af);
-        acc += part * (sa * sb);
     }
 
-    reinterpret_cast<v4f *>(&a_lds[wave][0])[lane] = acc;
+    // Wave w's partials of pass q sit at its area + 1 KB q; wave q reduces pass q.
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+#pragma unroll
+    for (int pass = 0; pass < MP; ++pass)
+        reinterpret_cast<v4f *>(&a_lds[wave][1024 * pass])[lane] = acc[pass];
     __syncthreads();
-    if (wave == 0) {
-        v4f v = reinterpret_cast<const v4f *>(&a_lds[0][0])[lane];
+    if (wave < MP) {
+        const int pass = wave;
+        v4f v = reinterpret_cast<const v4f *>(&a_lds[0][1024 * pass])[lane];
 #pragma unroll
         for (int w = 1; w < kDecodeWaves; ++w)
-            v += reinterpret_cast<const v4f *>(&a_lds[w][0])[lane];
-        if (arow)
-            *reinterpret_cast<uint2 *>(p.D + (int64_t)l16 * p.ldd + n0 + 4 * lg) = pack_bf16x4(v);
+            v += reinterpret_cast<const v4f *>(&a_lds[w][1024 * pass])[lane];
+        const int row = MR * pass + l16;
+        if (row < M)
+            *reinterpret_cast<uint2 *>(p.D + (int64_t)row * p.ldd + n0 + 4 * lg) = pack_bf16x4(v);
     }
 }
 

@@ -86,7 +86,8 @@ int dg_last_hip_error(void);
  * Operation as in the header comment (lpnh.cn §2.3; hotdry.top, fine-grained
  * scaling core design).
  *
- * Split-K: when 24 < M (64 < M for K < 2048) and the output tiles would fill at most half of the
+ * Split-K: when M > 64 (or 24 < M <= 64 where the small-M kernel's LDS
+ * staging does not fit and K >= 2048) and the output tiles would fill at most half of the
  * GPU's CUs (e.g. M up to ~2000 at N = 4096), each tile's K blocks are split
  * over up to 8 work items that write fp32 partial sums to a device workspace,
  * and a second kernel adds them in a fixed order. The workspace (slices x M x
