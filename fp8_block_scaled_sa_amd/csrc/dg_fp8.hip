@@ -233,7 +233,9 @@ bool launch_decode_dma(const dgk::Params &p, int nb, bool full, hipStream_t stre
     bool done = false;
     auto one = [&](auto nb_c) {
         constexpr int NB = decltype(nb_c)::value;
-        if constexpr (decode_dma_lds(NB, MR) <= 160 * 1024 && MP * 1024 <= NB * MR * 128) {
+        // more than 8 blocks per wave only in one pass (B fragments are not
+        // kept in registers across passes then)
+        if constexpr (decode_dma_lds(NB, MR) <= 160 * 1024 && MP * 1024 <= NB * MR * 128 && (MP == 1 || NB <= 8)) {
             if (nb != NB)
                 return;
             if (full)
@@ -251,6 +253,13 @@ bool launch_decode_dma(const dgk::Params &p, int nb, bool full, hipStream_t stre
     one(std::integral_constant<int, 6>{});
     one(std::integral_constant<int, 7>{});
     one(std::integral_constant<int, 8>{});
+    one(std::integral_constant<int, 9>{});
+    one(std::integral_constant<int, 10>{});
+    one(std::integral_constant<int, 11>{});
+    one(std::integral_constant<int, 12>{});
+    one(std::integral_constant<int, 13>{});
+    one(std::integral_constant<int, 14>{});
+    one(std::integral_constant<int, 15>{});
     return done;
 }
 
@@ -265,7 +274,7 @@ int launch_decode(dgk::Params &p, hipStream_t stream, bool fallback)
     const int grid = p.N / 16;
     hipError_t e;
     const int64_t nkb = p.K / 128;
-    const bool dma_ok = nkb % dgk::kDecodeWaves == 0 && nkb / dgk::kDecodeWaves <= 8 &&
+    const bool dma_ok = nkb % dgk::kDecodeWaves == 0 && nkb / dgk::kDecodeWaves <= 15 &&
                         (tile_override() < 7 || tile_override() > 9) &&
                         (int64_t)(p.M - 1) * p.lda + p.K < ((int64_t)1 << 31) &&
                         ((int64_t)(p.M - 1) * p.sa_m + (nkb - 1) * p.sa_kb) * 4 < ((int64_t)1 << 31);

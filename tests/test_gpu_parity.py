@@ -23,6 +23,7 @@ pytestmark = pytest.mark.gpu
     (777, 1152, 1280),
     (9, 256, 2048), (12, 384, 7168), (16, 512, 1024), (16, 128, 7168),   # 16-row LHS staging
     (17, 256, 1024), (24, 512, 1024), (32, 256, 7168), (48, 384, 2048), (64, 128, 4096),  # 2-4 passes
+    (8, 256, 14336), (5, 128, 12288), (16, 256, 9216),   # long K: 12-14 blocks per wave; M=16 falls back
 ])
 def test_dense_full_parity(gpu_device, M, N, K):
     p = gen.make_dense(M, N, K, 1000 + M, 2000 + N)
