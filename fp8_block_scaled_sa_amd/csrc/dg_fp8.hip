@@ -153,7 +153,8 @@ using CfgNarrow = dgk::TileCfg<128, 128, 2, 2, 4, 8>;
 // decode kernels; 12: masked B loaded without the non-temporal hint; 13 / 14:
 // decode kernels up to M = 16 / all older decode kernels up to 64; 15:
 // split-K always on 256-wide tiles;
-// 16: no split-K; 2, 3, 4 also pick the contiguous layout's tile shape.
+// 16: no split-K; 18: no cut of a partly filled last round of 256x256 tiles;
+// 2, 3, 4 also pick the contiguous layout's tile shape.
 int tile_override()
 {
     static int v = [] {
@@ -210,6 +211,73 @@ int launch_dense(dgk::Params &p, int cus, hipStream_t stream)
                        p.ws, ks, p.M, p.N, p.D, p.ldd);
     hipError_t e = hipGetLastError();
     return e == hipSuccess ? DG_OK : fail_hip(e);
+}
+
+// Rounds of 256x256 tiles: when the last round of a tiles_m x tiles_n grid
+// would be at most half full, the grid can be cut into a part of whole
+// rounds and a strip that a second launch covers with smaller tiles (the
+// per-element arithmetic does not depend on the tile shape). Returns the
+// number of leading n-tiles (cut_n) or else m-tiles (cut_m) of the
+// whole-round part, or 0 for no cut. Only dense grids are cut: on the
+// contiguous layout a row cut measured slower than the partly filled round.
+struct TileCut {
+    int64_t cut_n = 0, cut_m = 0;
+};
+TileCut round_cut(int64_t tiles_m, int64_t tiles_n, int cus)
+{
+    TileCut c;
+    const int64_t tiles = tiles_m * tiles_n;
+    const int64_t tail = tiles % cus;
+    if (tile_override() == 18 || tiles < cus || tail == 0 || tail * 2 > cus)
+        return c;
+    for (int64_t n1 = tiles_n - 1; n1 > 0; --n1)
+        if ((tiles_m * n1) % cus == 0) {
+            c.cut_n = n1;
+            return c;
+        }
+    for (int64_t m1 = tiles_m - 1; m1 > 0; --m1)
+        if ((m1 * tiles_n) % cus == 0) {
+            c.cut_m = m1;
+            return c;
+        }
+    return c;
+}
+
+// Dense GEMM, configuration chosen from the shape: 256x256 tiles while they
+// fill the CUs (a last round at most half full is cut off and run with
+// smaller tiles); below that, smaller tiles split over K.
+int launch_dense_auto(dgk::Params &p, int cus, hipStream_t s)
+{
+    const bool wide_n = p.N % 256 == 0;
+    const int64_t tiles_m = (p.M + 255) / 256, tiles_n = p.N / 256;
+    if (wide_n && tiles_m * tiles_n * 2 > cus) {
+        const TileCut c = round_cut(tiles_m, tiles_n, cus);
+        if (c.cut_n == 0 && c.cut_m == 0)
+            return launch_dense<CfgBig>(p, cus, s);
+        dgk::Params main = p, rest = p;
+        if (c.cut_n) {  // columns [0, N1) whole rounds; the rest on 256x128 tiles
+            const int64_t N1 = 256 * c.cut_n;
+            main.N = (int)N1;
+            rest.B += N1 * p.ldb;
+            rest.sB += (N1 / 128) * p.sb_nb;
+            rest.D += N1;
+            rest.N = p.N - (int)N1;
+        } else {        // rows [0, M1) whole rounds
+            const int64_t M1 = 256 * c.cut_m;
+            main.M = (int)M1;
+            rest.A += M1 * p.lda;
+            rest.sA += M1 * p.sa_m;
+            rest.D += M1 * p.ldd;
+            rest.M = p.M - (int)M1;
+        }
+        const int st = launch_dense<CfgBig>(main, cus, s);
+        if (st != DG_OK)
+            return st;
+        return c.cut_n ? launch_dense<CfgDense>(rest, cus, s) : launch_dense_auto(rest, cus, s);
+    }
+    if (p.M <= 128)
+        return launch_dense<CfgNarrow>(p, cus, s);
+    return launch_dense<CfgDense>(p, cus, s);
 }
 
 // Per-lane DMA offsets are 32-bit: a tile's rows of A, B and sA must span < 2^32 bytes.
@@ -392,16 +460,8 @@ int dg_fp8_gemm_nt(const void *A, int64_t lda, const float *sA, int64_t sa_strid
     case 2: return launch_tiles<dgk::kDense, CfgNarrow>(p, 1, dev.cus, s);
     case 4: return launch_tiles<dgk::kDense, CfgDense>(p, 1, dev.cus, s);
     case 15: return wide_n ? launch_dense<CfgBig>(p, dev.cus, s) : launch_dense<CfgDense>(p, dev.cus, s);
-    default: {
-        // 256x256 tiles while they fill the CUs; below that, smaller tiles
-        // split over K (more work items per byte of partial sums).
-        const int64_t big_tiles = ((M + 255) / 256) * (N / 256);
-        if (wide_n && big_tiles * 2 > dev.cus)
-            return launch_dense<CfgBig>(p, dev.cus, s);
-        if (M <= 128)
-            return launch_dense<CfgNarrow>(p, dev.cus, s);
-        return launch_dense<CfgDense>(p, dev.cus, s);
-    }
+    default:
+        return launch_dense_auto(p, dev.cus, s);
     }
 }
 

@@ -99,6 +99,12 @@ int dg_last_hip_error(void);
  * eager call on the capture stream beforehand puts the split in the graph).
  * Concurrent calls on different streams use different workspaces. If the
  * allocation fails the call runs without the split.
+ *
+ * Large grids: when the 256x256 output tiles fill the CUs but leave a last
+ * round at most half full, the call is issued as two launches on the same
+ * stream, the whole-round part of the columns (else rows) on 256x256 tiles
+ * and the remaining strip on smaller tiles (split over K if that strip alone
+ * is small). The cut depends only on the shape and the CU count.
  */
 int dg_fp8_gemm_nt(const void *A, int64_t lda,
                    const float *sA, int64_t sa_stride_m, int64_t sa_stride_kb,

@@ -66,6 +66,23 @@ def test_large_dense_sampled_parity(gpu_device, name):
     assert_close(got[ms, ns], ref, name)
 
 
+@pytest.mark.parametrize("M,N", [(4096, 4352), (4352, 4096)])
+def test_round_cut_sampled_parity(gpu_device, M, N):
+    # 272 tiles of 256x256 leave a last round of 16 on 256 CUs: the first
+    # 4096 columns (rows) run as whole rounds and the remaining strip as a
+    # second launch on smaller tiles. Every element written; sampled points
+    # (with whole rows and columns on both sides of the cut) against the oracle.
+    p = gen.make_dense(M, N, 512, 5000 + M, 6000 + N)
+    got = run_dense(p.a, p.sa_t.T, p.b, p.sb)
+    assert not np.any(got == SENTINEL), "every output element is written"
+    ms, ns = sample_points(p.M, p.N, 20000, 9)
+    cut_m = np.concatenate([np.full(N, 4095), np.full(N, min(4096, M - 1))])
+    cut_n = np.concatenate([np.arange(N), np.arange(N)])
+    ms, ns = np.concatenate([ms, cut_m, np.arange(M), np.arange(M)]), np.concatenate([ns, cut_n, np.full(M, 4095), np.full(M, min(4096, N - 1))])
+    ref, _ = oracle.gemm_nt_points(p.a, p.sa_t.T, p.b, p.sb, ms, ns)
+    assert_close(got[ms, ns], ref, "round cut %dx%d" % (M, N))
+
+
 @pytest.mark.parametrize("N", [384, 512])   # 256x128 and 256x256 tiles
 def test_small_contiguous_full_parity(gpu_device, N):
     # Segments of 1, 3, 1, 2 and 1 128-row blocks: three of the four 256-row
