@@ -161,6 +161,16 @@ __device__ __forceinline__ void dma_buf_b128_nt(const v4i &rsrc, uint32_t voff, 
                  : "memory", "m0");
 }
 
+// v + s, computed where it is written: the compiler cannot hoist it out of
+// the K loop, so the per-segment DMA offsets are not all kept live in VGPRs
+// (one add per copy instead of one VGPR per segment).
+__device__ __forceinline__ uint32_t add_in_place(uint32_t v, uint32_t s)
+{
+    uint32_t r;
+    asm volatile("v_add_u32 %0, %1, %2" : "=v"(r) : "s"(s), "v"(v));
+    return r;
+}
+
 template <int N>
 __device__ __forceinline__ void wait_vmcnt()
 {
@@ -248,7 +258,10 @@ struct TileCfg {
     // first) wave starts its MFMAs right after the barrier, and the copies'
     // issue stalls land on the wave that would otherwise wait for it there.
     static constexpr bool kDmaUpper = STAGES == 2 && ((BM + BN) / 8) % (WAVES_M * WAVES_N / 2) == 0;
-    static constexpr int kDmaQ = kDmaUpper ? 2 * ((BM + BN) / 8) / (WAVES_M * WAVES_N) : ((BM + BN) / 8) / (WAVES_M * WAVES_N);
+    static constexpr int kDmaWaves = kDmaUpper ? WAVES_M * WAVES_N / 2 : WAVES_M * WAVES_N;  // waves issuing copies
+    static constexpr int kDmaQ = ((BM + BN) / 8) / kDmaWaves;  // 1 KB segments per issuing wave
+    static constexpr int kDmaQA = (BM / 8) / kDmaWaves;        // of which A segments
+    static_assert((BM / 8) % kDmaWaves == 0, "A and B segments split evenly over the issuing waves");
     static_assert(kWM % 16 == 0 && kWN % 16 == 0, "wave tile");
     static_assert((kSegA + kSegB) % kWaves == 0, "segments split evenly over waves");
     static_assert(BM % 64 == 0 && kSaLoads <= kWaves, "sA loads");
@@ -381,22 +394,37 @@ __global__ void __launch_bounds__(C::kThreads, 1) tile_kernel(Params p)
         const uint32_t voff_sa = (uint32_t)(min(wave * 64 + lane, rows - 1) * p.sa_m * 4);
         const uint32_t voff_sb = (uint32_t)(min(lane, C::kNB - 1) * p.sb_nb * 4);
 
+        // Issuing wave w (of kDmaWaves) copies segments w, w + kDmaWaves, ...:
+        // its A segments first, then its B segments. The lane offset walks
+        // through them by one add per copy (see add_in_place).
+        const int w_dma = C::kDmaUpper ? wave - C::kWaves / 2 : wave;
+        const uint32_t va0 = voff_a + (uint32_t)(w_dma * 8 * p.lda);
+        const uint32_t vb0 = voff_b + (uint32_t)(w_dma * 8 * p.ldb);
+        const uint32_t step_a = (uint32_t)(C::kDmaWaves * 8 * p.lda);
+        const uint32_t step_b = (uint32_t)(C::kDmaWaves * 8 * p.ldb);
         auto issue = [&](int kb, int stage) {
             const uint32_t sbase = smem_base + stage * C::kStageBytes;
+            const uint32_t seg0 = sbase + w_dma * 1024;  // this wave's first segment
+            if (C::kDmaUpper && wave < C::kWaves / 2) {
+                // the lower half of the waves issues no operand copies
+            } else {
+                uint32_t o = va0;
 #pragma unroll
-            for (int q = 0; q < C::kDmaQ; ++q) {
-                // kDmaUpper: the upper half of the waves issues all segments.
-                const int seg = C::kDmaUpper ? q * (C::kWaves / 2) + (wave - C::kWaves / 2) : q * C::kWaves + wave;
-                if (C::kDmaUpper && wave < C::kWaves / 2)
-                    break;
-                if (seg < C::kSegA)
-                    dma_buf_b128(rsrc_a, voff_a + (uint32_t)(seg * 8 * p.lda), kb * 128, sbase + seg * 1024);
-                else if (C::kStreamB)
-                    dma_buf_b128_nt(rsrc_b, voff_b + (uint32_t)((seg - C::kSegA) * 8 * p.ldb), kb * 128,
-                                    sbase + seg * 1024);
-                else
-                    dma_buf_b128(rsrc_b, voff_b + (uint32_t)((seg - C::kSegA) * 8 * p.ldb), kb * 128,
-                                 sbase + seg * 1024);
+                for (int q = 0; q < C::kDmaQA; ++q) {
+                    dma_buf_b128(rsrc_a, o, kb * 128, seg0 + q * C::kDmaWaves * 1024);
+                    if (q + 1 < C::kDmaQA)
+                        o = add_in_place(o, step_a);
+                }
+                o = vb0;
+#pragma unroll
+                for (int q = C::kDmaQA; q < C::kDmaQ; ++q) {
+                    if (C::kStreamB)
+                        dma_buf_b128_nt(rsrc_b, o, kb * 128, seg0 + q * C::kDmaWaves * 1024);
+                    else
+                        dma_buf_b128(rsrc_b, o, kb * 128, seg0 + q * C::kDmaWaves * 1024);
+                    if (q + 1 < C::kDmaQ)
+                        o = add_in_place(o, step_b);
+                }
             }
             if (loads_sa)
                 dma_b32(sAb + (int64_t)kb * p.sa_kb, voff_sa, sbase + C::kOffSa + wave * 256);
