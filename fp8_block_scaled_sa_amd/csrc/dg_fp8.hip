@@ -306,7 +306,9 @@ bool launch_decode_dma(const dgk::Params &p, int nb, bool full, hipStream_t stre
         if constexpr (decode_dma_lds(NB, MR) <= 160 * 1024 && MP * 1024 <= NB * MR * 128 && (MP == 1 || NB <= 8)) {
             if (nb != NB)
                 return;
-            if (full)
+            if (full && (p.ldb & 4095) == 0)   // rotated block order (see the kernel)
+                hipLaunchKernelGGL((dgk::decode_dma_kernel<NB, MR, true, MP, true>), g, b, 0, stream, p);
+            else if (full)
                 hipLaunchKernelGGL((dgk::decode_dma_kernel<NB, MR, true, MP>), g, b, 0, stream, p);
             else
                 hipLaunchKernelGGL((dgk::decode_dma_kernel<NB, MR, false, MP>), g, b, 0, stream, p);

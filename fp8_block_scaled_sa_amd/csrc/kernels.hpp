@@ -872,7 +872,7 @@ __global__ void __launch_bounds__(kDecodeThreads, 1) decode_static_kernel(Params
 // sB and issues its B blocks (the HBM stream) straight into MFMA operand
 // registers. No barrier precedes the math: a wave only reads its own LDS
 // region, and each block's MFMA waits for that block's B alone.
-template <int NB, int MR, bool BFULL, int MP = 1>
+template <int NB, int MR, bool BFULL, int MP = 1, bool ROT = false>
 __global__ void __launch_bounds__(kDecodeThreads, 1) decode_dma_kernel(Params p)
 {
     // MP passes of MR = 16 LHS rows each (M <= 16 MP): B is loaded and put
@@ -898,6 +898,14 @@ __global__ void __launch_bounds__(kDecodeThreads, 1) decode_dma_kernel(Params p)
     const int n0 = blockIdx.x * 16;
     const int kb0 = wave * NB;
     const int M = p.M;
+    // ROT (chosen when B's row stride is a multiple of 4 KB): every row then
+    // starts at the same HBM channel offset, and the loads issued together
+    // would all sit at the same few 128-byte positions of a row, so
+    // workgroup g walks its waves' blocks starting at block g % NB
+    // (8x4096x4096: 6.25 -> 5.72 us). Without ROT the block indices stay
+    // compile-time constants. Only the order of the fp32 sum over blocks
+    // depends on it (fixed for a given shape).
+    const int rot = ROT ? (int)(blockIdx.x % NB) : 0;
 
     // 1. LHS rows [16 pass, 16 pass + MR): op q covers rows 8(q%(MR/8))..+7 of
     // block q/(MR/8); lane i takes row +i/8, physical chunk i%8 = logical
@@ -936,19 +944,21 @@ __global__ void __launch_bounds__(kDecodeThreads, 1) decode_dma_kernel(Params p)
     if constexpr (BFULL) {
         const uint8_t *bbase = p.B + (int64_t)(n0 + (lane >> 3)) * p.ldb + (int64_t)kb0 * 128 + 16 * (lane & 7);
 #pragma unroll
-        for (int u = 0; u < NB; ++u) {
+        for (int v = 0; v < NB; ++v) {
+            const int u = v + rot < NB ? v + rot : v + rot - NB;
 #pragma unroll
             for (int j = 0; j < 2; ++j)
-                bl[u][j] = __builtin_nontemporal_load(
+                bl[v][j] = __builtin_nontemporal_load(
                     reinterpret_cast<const v4u *>(bbase + (int64_t)(8 * j) * p.ldb + u * 128));
             __builtin_amdgcn_sched_barrier(0);  // keep block order: each block waits for itself only
         }
     } else {
         const uint8_t *brow = p.B + (int64_t)(n0 + l16) * p.ldb + (int64_t)kb0 * 128 + 16 * lg;
 #pragma unroll
-        for (int u = 0; u < NB; ++u) {
+        for (int v = 0; v < NB; ++v) {
+            const int u = v + rot < NB ? v + rot : v + rot - NB;
             const uint8_t *src = brow + u * 128;
-            bf[u] = join(*reinterpret_cast<const uint4 *>(src), *reinterpret_cast<const uint4 *>(src + 64));
+            bf[v] = join(*reinterpret_cast<const uint4 *>(src), *reinterpret_cast<const uint4 *>(src + 64));
         }
     }
     __builtin_amdgcn_sched_barrier(0);
@@ -972,17 +982,18 @@ __global__ void __launch_bounds__(kDecodeThreads, 1) decode_dma_kernel(Params p)
         acc[pass] = v4f{0.f, 0.f, 0.f, 0.f};
         const bool arow = MR * pass + l16 < M;
 #pragma unroll
-        for (int u = 0; u < NB; ++u) {
+        for (int v = 0; v < NB; ++v) {
+            const int u = v + rot < NB ? v + rot : v + rot - NB;  // block of the wave's range
             if constexpr (BFULL) {
                 if (pass == 0) {
-                    uint8_t *slot = &b_ring[wave][u & 1][0];
+                    uint8_t *slot = &b_ring[wave][v & 1][0];
 #pragma unroll
                     for (int j = 0; j < 2; ++j) {
                         const int r = 8 * j + (lane >> 3);
-                        *reinterpret_cast<v4u *>(slot + r * 128 + (((lane & 7) ^ swz(r)) << 4)) = bl[u][j];
+                        *reinterpret_cast<v4u *>(slot + r * 128 + (((lane & 7) ^ swz(r)) << 4)) = bl[v][j];
                     }
                     const uint8_t *t = slot + l16 * 128;
-                    bf[u] = join(*reinterpret_cast<const uint4 *>(t + ((lg ^ fsw) << 4)),
+                    bf[v] = join(*reinterpret_cast<const uint4 *>(t + ((lg ^ fsw) << 4)),
                                  *reinterpret_cast<const uint4 *>(t + (((lg + 4) ^ fsw) << 4)));
                 }
             }
@@ -995,7 +1006,7 @@ __global__ void __launch_bounds__(kDecodeThreads, 1) decode_dma_kernel(Params p)
                 sa = sa_lds[wave][u * MR + l16];
             }
             const float sb = __shfl(sbv, u);
-            const v4f part = mfma_e4m3_16x16x128(bf[u], af);
+            const v4f part = mfma_e4m3_16x16x128(bf[v], af);
             acc[pass] += part * (sa * sb);
         }
     }

@@ -24,6 +24,7 @@ pytestmark = pytest.mark.gpu
     (9, 256, 2048), (12, 384, 7168), (16, 512, 1024), (16, 128, 7168),   # 16-row LHS staging
     (17, 256, 1024), (24, 512, 1024), (32, 256, 7168), (48, 384, 2048), (64, 128, 4096),  # 2-4 passes
     (8, 256, 14336), (5, 128, 12288), (16, 256, 9216),   # long K: 12-14 blocks per wave; M=16 falls back
+    (8, 512, 4096), (5, 384, 8192), (16, 256, 4096), (40, 256, 8192),  # 4 KB row strides: rotated block order
 ])
 def test_dense_full_parity(gpu_device, M, N, K):
     p = gen.make_dense(M, N, K, 1000 + M, 2000 + N)
