@@ -552,29 +552,68 @@ __global__ void __launch_bounds__(C::kThreads, 1) tile_kernel(Params p)
             acc[MI - 1][j] += part[j] * part_sc;
 
         uint16_t *Dg = p.D + (int64_t)g * p.d_stride_g;
-#pragma unroll
-        for (int i = 0; i < MI; ++i) {
-            const int m = m0 + wm0 + 16 * i + l16;
-            bool ok;
+        auto row_ok = [&](int m) {
             if (L == kDense)
-                ok = m < p.M;
-            else if (L == kMasked)
-                ok = m < limit;
-            else
-                ok = m < p.M && p.ids[m] == expert;
-            if (!ok)
-                continue;
-            if (ks > 1) {
+                return m < p.M;
+            if (L == kMasked)
+                return m < limit;
+            return m < p.M && p.ids[m] == expert;
+        };
+        if (ks > 1) {
+#pragma unroll
+            for (int i = 0; i < MI; ++i) {
+                const int m = m0 + wm0 + 16 * i + l16;
+                if (!row_ok(m))
+                    continue;
                 float *wrow = p.ws + ((int64_t)slice * p.M + m) * p.N + n0 + wn0 + 4 * lg;
 #pragma unroll
                 for (int j = 0; j < NJ; ++j)
                     *reinterpret_cast<v4f *>(wrow + 16 * j) = acc[i][j];
-                continue;
             }
-            uint16_t *drow = Dg + (int64_t)m * p.ldd + n0 + wn0 + 4 * lg;
+            continue;
+        }
+        if constexpr (L == kContiguous) {
+            // Direct stores (8 bytes per lane): staging through LDS made the
+            // contiguous kernel spill in its K loop.
 #pragma unroll
-            for (int j = 0; j < NJ; ++j)
-                *reinterpret_cast<uint2 *>(drow + 16 * j) = pack_bf16x4(acc[i][j]);
+            for (int i = 0; i < MI; ++i) {
+                const int m = m0 + wm0 + 16 * i + l16;
+                if (!row_ok(m))
+                    continue;
+                uint16_t *drow = Dg + (int64_t)m * p.ldd + n0 + wn0 + 4 * lg;
+#pragma unroll
+                for (int j = 0; j < NJ; ++j)
+                    *reinterpret_cast<uint2 *>(drow + 16 * j) = pack_bf16x4(acc[i][j]);
+            }
+            continue;
+        }
+        // bf16 results go through this wave's own LDS area (the stages are
+        // free once every wave is past its last block), so that each store
+        // instruction writes whole rows of the wave's tile: RPI rows of RB
+        // bytes, 16 bytes per lane. Chunks are XOR-permuted by row & 7.
+        constexpr int RB = C::kWN * 2, CPR = RB / 16, RPI = 64 / CPR;
+        static_assert(C::kWaves * C::kWM * RB <= C::kSmemBytes, "epilogue staging fits the stages");
+        static_assert(CPR >= 8 && 64 % CPR == 0, "epilogue row layout");
+        uint8_t *ep = smem + wave * (C::kWM * RB);
+        wg_barrier();
+#pragma unroll
+        for (int i = 0; i < MI; ++i) {
+            const int r = 16 * i + l16;
+#pragma unroll
+            for (int j = 0; j < NJ; ++j) {
+                const int c = 2 * j + (lg >> 1);
+                *reinterpret_cast<uint2 *>(ep + r * RB + ((c ^ (r & 7)) << 4) + ((lg & 1) << 3)) =
+                    pack_bf16x4(acc[i][j]);
+            }
+        }
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // own area: no barrier needed
+#pragma unroll
+        for (int q = 0; q < C::kWM / RPI; ++q) {
+            const int r = q * RPI + lane / CPR, c = lane % CPR;
+            const uint4 v = *reinterpret_cast<const uint4 *>(ep + r * RB + ((c ^ (r & 7)) << 4));
+            const int m = m0 + wm0 + r;
+            if (row_ok(m))
+                *reinterpret_cast<uint4 *>(Dg + (int64_t)m * p.ldd + n0 + wn0 + c * 8) = v;
         }
         }  // pass
     }
