@@ -47,6 +47,9 @@ def lib():
         _lib.dgo_block_partial.restype = ctypes.c_double
         _lib.dgo_block_partial.argtypes = [_p, _p]
         _lib.dgo_max_threads.restype = ctypes.c_int
+        _lib.dgo_e4m3_encode.restype = ctypes.c_uint8
+        _lib.dgo_e4m3_encode.argtypes = [ctypes.c_float]
+        _lib.dgo_quantize_1x128.restype = None
         for name in ("dgo_gemm_nt", "dgo_gemm_nt_points", "dgo_grouped_contiguous",
                      "dgo_grouped_contiguous_points", "dgo_grouped_masked",
                      "dgo_grouped_masked_points"):
@@ -208,6 +211,33 @@ def grouped_masked_points(a, sa_t, b, sb, masked_m, gs, ms, ns, threads=None):
                                     _ptr(gs), _ptr(ms), _ptr(ns), _i64(cnt),
                                     _ptr(acc), _ptr(d), _ptr(produced), _threads(threads))
     return d, acc, produced.astype(bool)
+
+
+def e4m3_encode(v: float) -> int:
+    """Nearest e4m3 code (ties to even) of the fp32 value ``v`` clamped to +-448."""
+    return int(lib().dgo_e4m3_encode(float(v)))
+
+
+def quantize_1x128(x, threads=None):
+    """1x128 block quantisation of activations ``x [M, K]``: fp32, or bf16 given
+    as a torch bfloat16 tensor or as uint16 bit patterns. Returns
+    ``(codes [M, K] u8, scales [M, K/128] fp32)``."""
+    try:
+        import torch
+        if isinstance(x, torch.Tensor):
+            x = (x.contiguous().view(torch.int16).numpy().view(np.uint16)
+                 if x.dtype == torch.bfloat16 else x.contiguous().numpy())
+    except ImportError:
+        pass
+    is_bf16 = x.dtype == np.uint16
+    x = np.ascontiguousarray(x, dtype=np.uint16 if is_bf16 else np.float32)
+    M, K = x.shape
+    assert K % 128 == 0
+    q = np.zeros((M, K), dtype=np.uint8)
+    s = np.zeros((M, K // 128), dtype=np.float32)
+    lib().dgo_quantize_1x128(_ptr(x), ctypes.c_int(int(is_bf16)), _i64(K), _i64(M), _i64(K),
+                             _ptr(q), _i64(K), _ptr(s), _i64(K // 128), _i64(1), _threads(threads))
+    return q, s
 
 
 def _strided(s: np.ndarray):

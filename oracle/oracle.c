@@ -307,3 +307,76 @@ void dgo_grouped_masked_points(const uint8_t *A, int64_t lda, int64_t a_stride_g
         d[i] = dgo_bf16_rne(v);
     }
 }
+
+/* ------------------------------------------------------------------------
+ * 1x128 activation quantiser: the step that produces the GEMM's LHS codes
+ * and scales from fp32 (or bf16) activations.
+ *
+ * Per row m and 128-wide K block kb (one LHS scale per 1x128 tile: hotdry.top,
+ * "fine-grained scaling core design"):
+ *   amax = max |x[m, k]| over the block;
+ *   s    = amax / 448 as an fp32 division (the initial scale max_val / 448 of
+ *          the rkmt.cn walkthrough, §5.2), or s = 1 when amax == 0;
+ *   q    = e4m3 code nearest to clamp(x / s, -448, 448), x / s an fp32
+ *          division, ties to the even code (round to nearest rather than
+ *          toward zero: lpnh.cn article, §6.3).
+ * The sign of a value that rounds to zero is kept (code 0x80 for negatives).
+ * Inputs are finite.
+ * ------------------------------------------------------------------------ */
+
+/* Nearest e4m3 code to v (|v| <= 448 after the clamp), found by comparing v
+ * with every finite non-negative code 0x00..0x7E; on a tie the code with an
+ * even mantissa (even code) wins. */
+uint8_t dgo_e4m3_encode(float v)
+{
+    init_table();
+    double a = fabs((double)v);
+    if (a > 448.0)
+        a = 448.0;
+    int best = 0;
+    double best_err = a;                    /* distance to code 0x00 (zero) */
+    for (int c = 1; c <= 0x7E; ++c) {
+        double err = fabs(dec_table[c] - a);
+        if (err < best_err || (err == best_err && (c & 1) == 0 && (best & 1) == 1)) {
+            best = c;
+            best_err = err;
+        }
+    }
+    return (uint8_t)(signbit(v) ? (0x80 | best) : best);
+}
+
+static float load_x(const void *X, int is_bf16, int64_t i)
+{
+    if (is_bf16) {
+        uint32_t bits = (uint32_t)((const uint16_t *)X)[i] << 16;   /* bf16 is the top half of fp32 */
+        float f;
+        memcpy(&f, &bits, 4);
+        return f;
+    }
+    return ((const float *)X)[i];
+}
+
+/* X [M, K] (fp32, or bf16 bits when is_bf16), row stride ldx elements.
+ * Q [M, K] codes, row stride ldq. S[m, kb] at S[m*s_m + kb*s_kb]. */
+void dgo_quantize_1x128(const void *X, int is_bf16, int64_t ldx, int64_t M, int64_t K,
+                        uint8_t *Q, int64_t ldq, float *S, int64_t s_m, int64_t s_kb, int threads)
+{
+    init_table();
+    set_threads(threads);
+#pragma omp parallel for collapse(2) schedule(static)
+    for (int64_t m = 0; m < M; ++m)
+        for (int64_t kb = 0; kb < K / BLK; ++kb) {
+            float amax = 0.0f;
+            for (int64_t k = kb * BLK; k < (kb + 1) * BLK; ++k) {
+                float a = fabsf(load_x(X, is_bf16, m * ldx + k));
+                if (a > amax)
+                    amax = a;
+            }
+            float s = (amax == 0.0f) ? 1.0f : amax / 448.0f;
+            for (int64_t k = kb * BLK; k < (kb + 1) * BLK; ++k) {
+                float v = load_x(X, is_bf16, m * ldx + k) / s;
+                Q[m * ldq + k] = dgo_e4m3_encode(v);
+            }
+            S[m * s_m + kb * s_kb] = s;
+        }
+}
