@@ -6,7 +6,9 @@ batch of synthetic inputs already resident in HBM. The headline workload is
 the decode-shaped dense GEMM M=8, N=4096, K=7168, which is bound by streaming
 B from HBM; its metric is HBM GB/s of algorithmic bytes (A + sA + B + sB + D,
 each counted once). The other workloads are timed the same way and reported
-under "workloads".
+under "workloads", together with the 1x128 activation quantiser that
+produces the GEMM's LHS (fp32 and bf16 token activations, 8192 x 7168;
+HBM GB/s of algorithmic bytes: input + codes + scales).
 
 Memory-bound workloads rotate over enough copies of their operands (> 2x the
 256 MB last-level cache) that every launch reads its B from HBM.
@@ -33,11 +35,14 @@ ROTATE_BYTES = 600 * 2 ** 20   # > 2x the 256 MB last-level cache
 HEADLINE = "decode_8x4096x7168"
 METRIC = "FP8 GEMM TFLOP/s (and HBM GB/s at small M) + % of MI355X roofline, 1 GPU"
 KERNEL_SOURCES = ["fp8_block_scaled_sa_amd/csrc/kernels.hpp", "fp8_block_scaled_sa_amd/csrc/dg_fp8.hip"]
+# The quantiser's source is hashed on its own, so its counters stay valid
+# while the GEMM kernels change, and the other way round.
+QUANT_SOURCES = ["fp8_block_scaled_sa_amd/csrc/quant.hpp"]
 
 
-def kernel_hash() -> str:
+def kernel_hash(sources=KERNEL_SOURCES) -> str:
     h = hashlib.sha256()
-    for f in KERNEL_SOURCES:
+    for f in sources:
         with open(os.path.join(ROOT, f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
@@ -165,6 +170,49 @@ def time_workload(name, steps, warmup, rotate=True):
                 tflops=flops / avg_kernel_s / 1e12, gbs=byts / avg_kernel_s / 1e9)
 
 
+def time_quant(name, steps, warmup):
+    """The 1x128 activation quantiser, timed like the GEMMs: eager warm-up, then
+    `steps` launches in one graph between HIP events on the launch stream,
+    rotating over enough input copies that every launch reads from HBM."""
+    import torch
+    from fp8_block_scaled_sa_amd import ops
+    from synth import gen
+    c = gen.QUANT_CONFIGS[name]
+    M, K = c["M"], c["K"]
+    x = torch.from_numpy(gen.make_activations(name))
+    if c["dtype"] == "bf16":
+        x = x.to(torch.bfloat16)
+    x = x.cuda()
+    n = max(1, min(8, -(-ROTATE_BYTES // (x.numel() * x.element_size()))))
+    xs = [x] + [x.clone() for _ in range(n - 1)]
+    q = torch.empty((M, K), dtype=torch.uint8, device="cuda")
+    s = torch.empty((K // 128, M), dtype=torch.float32, device="cuda").t()
+    run = lambda i: ops.dg_fp8_quantize_1x128(xs[i % n], q=q, s=s)  # noqa: E731
+    for i in range(warmup):
+        run(i)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    cap = torch.cuda.Stream()
+    cap.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.graph(graph, stream=cap):
+        for i in range(steps):
+            run(i)
+    graph.replay()
+    torch.cuda.synchronize()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record(cap)
+    with torch.cuda.stream(cap):
+        graph.replay()
+    end.record(cap)
+    torch.cuda.synchronize()
+    us = start.elapsed_time(end) * 1e3 / steps
+    byts = M * K * x.element_size() + M * K + M * (K // 128) * 4
+    del graph
+    return {"kernel_avg_us": round(us, 2), "gbs": round(byts / us / 1e3, 1),
+            "frac_hbm_peak": round(byts / us / 1e3 / HBM_PEAK_GBS, 4), "algorithmic_bytes": byts,
+            "traffic": load_traffic(name, QUANT_SOURCES), "input_copies": n}
+
+
 def cpu_baseline(name, p, byts, min_seconds=10.0):
     """The oracle, as it stands, on this host's cores: full passes over the
     workload, repeated until at least min_seconds of work have run (one pass if
@@ -183,14 +231,16 @@ def cpu_baseline(name, p, byts, min_seconds=10.0):
             "sample": "the full %s problem (all %d outputs), %d passes in %.1f s" % (name, p.M * p.N, passes, dt)}
 
 
-def load_traffic(kernel_name):
+def load_traffic(workload, sources=KERNEL_SOURCES):
+    """HBM bytes per launch from the committed FETCH_SIZE/WRITE_SIZE summary,
+    or None when the kernel sources changed since the counters were taken."""
     path = os.path.join(ROOT, "profiles", "traffic.json")
     if not os.path.exists(path):
         return None
     with open(path) as f:
         tr = json.load(f)
-    ent = tr.get(kernel_name)
-    if not ent or ent.get("kernel_hash") != kernel_hash():
+    ent = tr.get(workload)
+    if not ent or ent.get("kernel_hash") != kernel_hash(sources):
         return None
     return ent.get("bytes_per_launch")
 
@@ -243,8 +293,14 @@ def main():
 
     others = {}
     names = [] if args.others == "none" else (
-        [n for n in gen.CONFIGS if n != args.workload] if args.others == "all" else args.others.split(","))
+        [n for n in list(gen.CONFIGS) + list(gen.QUANT_CONFIGS) if n != args.workload]
+        if args.others == "all" else args.others.split(","))
     for n in names:
+        if n in gen.QUANT_CONFIGS:
+            # at least 50 timed launches: the graph's launch latency is spread over them
+            others[n] = time_quant(n, max(50, args.steps // 4), max(3, args.warmup // 4))
+            torch.cuda.empty_cache()
+            continue
         r = time_workload(n, max(10, args.steps // 10), max(3, args.warmup // 4))
         others[n] = {"kernel_avg_us": round(r["kernel_avg_us"], 2), "eager_med_us": round(r["eager_med_us"], 2),
                      "tflops": round(r["tflops"], 2), "gbs": round(r["gbs"], 1),
@@ -268,6 +324,7 @@ def main():
         "cpu_baseline": cpu,
         "workloads": others,
         "kernel_hash": kernel_hash(),
+        "quant_kernel_hash": kernel_hash(QUANT_SOURCES),
     }
     print(json.dumps(line), flush=True)
 

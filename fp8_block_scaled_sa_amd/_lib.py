@@ -22,6 +22,8 @@ SIGNATURES = {
     "dg_fp8_grouped_gemm_masked": (ctypes.c_int, [_p, _i64, _i64, _p, _i64, _i64, _i64,
                                                   _p, _i64, _i64, _p, _i64, _i64, _i64, _p,
                                                   _p, _i64, _i64, _i64, _i64, _i64, _i64, _p]),
+    "dg_fp8_quantize_1x128": (ctypes.c_int, [_p, ctypes.c_int, _i64, _p, _i64, _p, _i64, _i64,
+                                             _i64, _i64, _p]),
 }
 
 _lib = None

@@ -12,6 +12,7 @@
 
 #include "dg_fp8.h"
 #include "kernels.hpp"
+#include "quant.hpp"
 
 namespace {
 
@@ -582,6 +583,63 @@ int dg_fp8_grouped_gemm_masked(const void *A, int64_t lda, int64_t a_stride_g, c
             return launch_tiles<dgk::kMasked, CfgBigStreamB>(p, (int)G, dev.cus, (hipStream_t)stream);
         return launch_tiles<dgk::kMasked, CfgDense>(p, (int)G, dev.cus, (hipStream_t)stream);
     }
+}
+
+int dg_fp8_quantize_1x128(const void *X, int x_dtype, int64_t ldx, void *Q, int64_t ldq, float *S,
+                          int64_t s_stride_m, int64_t s_stride_kb, int64_t M, int64_t K, void *stream)
+{
+    if (M < 0 || K <= 0 || K % 128 != 0)
+        return DG_ERR_BAD_SHAPE;
+    if (x_dtype != DG_DTYPE_F32 && x_dtype != DG_DTYPE_BF16)
+        return DG_ERR_UNSUPPORTED;
+    if (M > kInt32Max || K > kInt32Max)
+        return DG_ERR_UNSUPPORTED;
+    if (M == 0)
+        return DG_OK;
+    if (!X || !Q || !S)
+        return DG_ERR_NULL_POINTER;
+    const int64_t nkb = K / 128;
+    // Every (m, kb) must own its scale: a row-major-like or an M-major-like
+    // layout (a dimension of extent 1 may take any stride).
+    const bool rows_distinct = M == 1 || s_stride_m >= 1;
+    const bool blocks_distinct = nkb == 1 || s_stride_kb >= 1;
+    const bool row_major = s_stride_m >= (nkb - 1) * s_stride_kb + 1 || M == 1;
+    const bool m_major = s_stride_kb >= (M - 1) * s_stride_m + 1 || nkb == 1;
+    if (ldx < K || ldq < K || s_stride_m < 0 || s_stride_kb < 0 || !rows_distinct || !blocks_distinct ||
+        !(row_major || m_major))
+        return DG_ERR_BAD_STRIDE;
+    const int64_t esize = x_dtype == DG_DTYPE_F32 ? 4 : 2;
+    if (!aligned(X, 16) || !aligned(Q, 16) || (ldx * esize) % 16 || ldq % 16 || !aligned(S, 4))
+        return DG_ERR_MISALIGNED;
+    const Extent ex = extent(X, esize, (M - 1) * ldx + K - 1);
+    const Extent eq = extent(Q, 1, (M - 1) * ldq + K - 1);
+    const Extent es = extent(S, 4, last_scale_index(M, nkb, s_stride_m, s_stride_kb));
+    if (overlaps(eq, ex) || overlaps(es, ex) || overlaps(eq, es))
+        return DG_ERR_ALIASING;
+    const int64_t span_len = 1024 * (x_dtype == DG_DTYPE_BF16 ? dgq::groups_per_wave<true>()
+                                                             : dgq::groups_per_wave<false>());
+    const int64_t spans = (K + span_len - 1) / span_len;
+    const int64_t units = M * spans;
+    const int64_t groups = (units + dgq::kWavesPerGroup - 1) / dgq::kWavesPerGroup;
+    if (groups > kInt32Max)
+        return DG_ERR_UNSUPPORTED;
+    DeviceInfo dev;
+    int st = current_device(dev);
+    if (st != DG_OK)
+        return st;
+
+    dgq::QuantParams p = {};
+    p.X = X; p.ldx = ldx;
+    p.Q = (uint8_t *)Q; p.ldq = ldq;
+    p.S = S; p.s_m = s_stride_m; p.s_kb = s_stride_kb;
+    p.M = (int)M; p.K = (int)K; p.spans = (int)spans; p.units = units;
+    const dim3 grid((unsigned)groups), block(64 * dgq::kWavesPerGroup);
+    if (x_dtype == DG_DTYPE_BF16)
+        hipLaunchKernelGGL(dgq::quantize_1x128_kernel<true>, grid, block, 0, (hipStream_t)stream, p);
+    else
+        hipLaunchKernelGGL(dgq::quantize_1x128_kernel<false>, grid, block, 0, (hipStream_t)stream, p);
+    const hipError_t e = hipGetLastError();
+    return e == hipSuccess ? DG_OK : fail_hip(e);
 }
 
 }  // extern "C"

@@ -135,3 +135,30 @@ def dg_fp8_grouped_gemm_masked(a, sa, b, sb, masked_m, d=None, stream=None):
         G, M_max, N, K, _stream(stream))
     _check(st, "dg_fp8_grouped_gemm_masked")
     return d
+
+
+DTYPES = {torch.float32: 0, torch.bfloat16: 1}   # DG_DTYPE_F32, DG_DTYPE_BF16
+
+
+def dg_fp8_quantize_1x128(x, q=None, s=None, stream=None):
+    """Codes Q[M,K] (uint8 e4m3) and scales S[M,K/128] (fp32) of activations
+    x[M,K] (float32 or bfloat16), one scale per 1x128 block. A new S is
+    M-major (stored [K/128, M], returned as its transposed view), the layout
+    the GEMM calls read fastest. Returns (q, s)."""
+    if x.dtype not in DTYPES:
+        raise TypeError("x must be float32 or bfloat16")
+    if x.dim() != 2 or x.stride(-1) != 1:
+        raise ValueError("x must be 2-D with a contiguous last (K) dimension")
+    M, K = x.shape
+    if q is None:
+        q = torch.empty((M, K), dtype=torch.uint8, device=x.device)
+    if s is None:
+        s = torch.empty((K // BLOCK, M), dtype=torch.float32, device=x.device).t()
+    _codes(q, "q", 2), _scales(s, "s", 2)
+    if tuple(q.shape) != (M, K) or tuple(s.shape) != (M, K // BLOCK):
+        raise ValueError("shape mismatch")
+    lib = _lib.load()
+    st = lib.dg_fp8_quantize_1x128(_dev(x, "x"), DTYPES[x.dtype], x.stride(0), _dev(q, "q"), q.stride(0),
+                                   _dev(s, "s"), s.stride(0), s.stride(1), M, K, _stream(stream))
+    _check(st, "dg_fp8_quantize_1x128")
+    return q, s

@@ -20,6 +20,9 @@
  *
  * "NT": A is [M, K] and B is [N, K], both with K contiguous, D = A . B^T.
  *
+ * dg_fp8_quantize_1x128 (at the end) produces A and sA from fp32 or bf16
+ * activations: the quantisation step that precedes the GEMM.
+ *
  * Conventions shared by every entry point
  *   - All pointers are DEVICE pointers owned by the caller; the library never
  *     keeps one past return.
@@ -161,6 +164,40 @@ int dg_fp8_grouped_gemm_masked(const void *A, int64_t lda, int64_t a_stride_g,
                                const int32_t *masked_m,
                                void *D, int64_t ldd, int64_t d_stride_g,
                                int64_t G, int64_t M_max, int64_t N, int64_t K, void *stream);
+
+/* Element types of the quantiser's input. */
+#define DG_DTYPE_F32 0
+#define DG_DTYPE_BF16 1
+
+/*
+ * 1x128 activation quantiser: produces the LHS of the calls above (codes and
+ * one scale per 1x128 tile: hotdry.top, "fine-grained scaling core design")
+ * from fp32 or bf16 activations.
+ *   X  [M, K] fp32 (x_dtype DG_DTYPE_F32) or bf16 (DG_DTYPE_BF16), row stride ldx elements
+ *   Q  [M, K] e4m3 codes, row stride ldq (written)
+ *   S  fp32 logical [M, K/128]: S[m, kb] at S[m*s_stride_m + kb*s_stride_kb] (written)
+ * For row m and block kb (columns [128 kb, 128 kb + 128)):
+ *   amax = max |X[m, k]| over the block;
+ *   s    = amax / 448 as an fp32 division (the initial scale max_val / 448 of
+ *          the rkmt.cn walkthrough, §5.2), or 1 when amax is 0;
+ *   Q    = the e4m3 code nearest to clamp(X / s, -448, 448), X / s an fp32
+ *          division, ties to the even code (round to nearest: lpnh.cn §6.3);
+ *          a negative value that rounds to zero gives -0 (0x80).
+ * So X ~ dec(Q) * s, and Q/S are directly the A/sA of the GEMM calls (pass
+ * sa_stride_m = s_stride_m, sa_stride_kb = s_stride_kb).
+ * Inputs must be finite; the codes and scale of a block holding NaN or
+ * infinity are unspecified (no fault).
+ * Constraints: K > 0, K % 128 == 0; X and Q 16-byte aligned, ldx * element
+ * size and ldq multiples of 16; S 4-byte aligned; ldx >= K, ldq >= K; every
+ * (m, kb) owns a distinct scale slot (row-major-like or M-major-like strides,
+ * >= 0); Q, S and X pairwise disjoint. Errors as for the GEMM calls, plus
+ * DG_ERR_UNSUPPORTED for an unknown x_dtype. Deterministic; M = 0 returns
+ * DG_OK without launching. Asynchronous on `stream`, allocates nothing.
+ */
+int dg_fp8_quantize_1x128(const void *X, int x_dtype, int64_t ldx,
+                          void *Q, int64_t ldq,
+                          float *S, int64_t s_stride_m, int64_t s_stride_kb,
+                          int64_t M, int64_t K, void *stream);
 
 #ifdef __cplusplus
 }

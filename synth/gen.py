@@ -232,6 +232,20 @@ CONFIGS = {
 }
 
 
+# Activations for the 1x128 quantiser: the token activations of the MoE
+# workloads (8192 tokens, hidden size 7168), fp32 or bf16.
+QUANT_CONFIGS = {
+    "quantize_f32_8192x7168": dict(M=8192, K=7168, dtype="f32", seed=701),
+    "quantize_bf16_8192x7168": dict(M=8192, K=7168, dtype="bf16", seed=702),
+}
+
+
+def make_activations(name: str) -> np.ndarray:
+    """fp32 activations of a quantiser workload (bf16 workloads round them)."""
+    c = QUANT_CONFIGS[name]
+    return normal_with_outliers(np.random.Generator(np.random.PCG64(c["seed"])), (c["M"], c["K"]))
+
+
 def make_config(name: str):
     c = CONFIGS[name]
     if c["kind"] == "dense":

@@ -24,6 +24,7 @@ def declared_symbols():
 def test_header_declares_the_entry_points():
     syms = declared_symbols()
     for name in ("dg_fp8_gemm_nt", "dg_fp8_grouped_gemm_contiguous", "dg_fp8_grouped_gemm_masked",
+                 "dg_fp8_quantize_1x128",
                  "dg_abi_version", "dg_status_string", "dg_last_hip_error"):
         assert name in syms
 
@@ -136,3 +137,53 @@ def test_masked_validation(kw, status):
 def test_masked_empty():
     assert masked(G=0) == DG_OK
     assert masked(M_max=0) == DG_OK
+
+
+X, Q, S = A, B, SB
+
+
+def quant(**kw):
+    args = dict(X=X, x_dtype=0, ldx=512, Q=Q, ldq=512, S=S, s_m=1, s_kb=64, M=64, K=512, stream=None)
+    args.update(kw)
+    return _lib.load().dg_fp8_quantize_1x128(*args.values())
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(K=500, ldx=512, ldq=512), DG_ERR_BAD_SHAPE),
+    (dict(K=0), DG_ERR_BAD_SHAPE),
+    (dict(M=-1), DG_ERR_BAD_SHAPE),
+    (dict(x_dtype=2), DG_ERR_UNSUPPORTED),
+    (dict(M=2 ** 31), DG_ERR_UNSUPPORTED),
+    (dict(X=None), DG_ERR_NULL_POINTER),
+    (dict(Q=None), DG_ERR_NULL_POINTER),
+    (dict(S=None), DG_ERR_NULL_POINTER),
+    (dict(ldx=256), DG_ERR_BAD_STRIDE),
+    (dict(ldq=384), DG_ERR_BAD_STRIDE),
+    (dict(s_m=-1), DG_ERR_BAD_STRIDE),
+    (dict(s_m=0), DG_ERR_BAD_STRIDE),          # rows would share a scale slot
+    (dict(s_m=1, s_kb=32), DG_ERR_BAD_STRIDE),  # M-major with a stride shorter than M
+    (dict(s_m=3, s_kb=1), DG_ERR_BAD_STRIDE),   # row-major with a stride shorter than K/128
+    (dict(X=X + 8), DG_ERR_MISALIGNED),
+    (dict(Q=Q + 4), DG_ERR_MISALIGNED),
+    (dict(ldx=514), DG_ERR_MISALIGNED),
+    (dict(x_dtype=1, ldx=516), DG_ERR_MISALIGNED),
+    (dict(ldq=520), DG_ERR_MISALIGNED),
+    (dict(S=S + 2), DG_ERR_MISALIGNED),
+    (dict(Q=X + 4096), DG_ERR_ALIASING),
+    (dict(S=X + 256), DG_ERR_ALIASING),
+    (dict(S=Q + 1024), DG_ERR_ALIASING),
+])
+def test_quantize_validation(kw, status):
+    assert quant(**kw) == status
+
+
+def test_quantize_accepts_both_scale_layouts_up_to_the_device_check():
+    # Valid arguments get past validation: on a machine without a GPU the call
+    # then fails at the device query, never with an argument error.
+    for kw in (dict(s_m=1, s_kb=64), dict(s_m=4, s_kb=1), dict(x_dtype=1, ldx=520)):
+        assert quant(**kw) in (DG_OK, DG_ERR_HIP, DG_ERR_UNSUPPORTED)
+
+
+def test_quantize_empty():
+    assert quant(M=0) == DG_OK
+    assert quant(M=0, X=None, Q=None, S=None) == DG_OK
