@@ -50,6 +50,8 @@ def lib():
         _lib.dgo_e4m3_encode.restype = ctypes.c_uint8
         _lib.dgo_e4m3_encode.argtypes = [ctypes.c_float]
         _lib.dgo_quantize_1x128.restype = None
+        _lib.dgo_moe_route_contiguous.restype = ctypes.c_int
+        _lib.dgo_moe_unpermute.restype = None
         for name in ("dgo_gemm_nt", "dgo_gemm_nt_points", "dgo_grouped_contiguous",
                      "dgo_grouped_contiguous_points", "dgo_grouped_masked",
                      "dgo_grouped_masked_points"):
@@ -238,6 +240,40 @@ def quantize_1x128(x, threads=None):
     lib().dgo_quantize_1x128(_ptr(x), ctypes.c_int(int(is_bf16)), _i64(K), _i64(M), _i64(K),
                              _ptr(q), _i64(K), _ptr(s), _i64(K // 128), _i64(1), _threads(threads))
     return q, s
+
+
+def moe_max_rows(T: int, G: int) -> int:
+    """Rows that always hold the padded contiguous layout of T tokens over G
+    experts: each used expert wastes fewer than 128 rows."""
+    return 128 * (-(-T // 128) + min(G, T))
+
+
+def moe_route_contiguous(expert_of_token, G, M_cap=None):
+    """Returns ``(row_of_token [T], expert_ids [M_cap], token_of_row [M_cap],
+    layout [G+1])`` as int32 arrays."""
+    e = np.ascontiguousarray(expert_of_token, dtype=np.int32)
+    T = e.shape[0]
+    M_cap = moe_max_rows(T, G) if M_cap is None else M_cap
+    row = np.zeros(T, np.int32)
+    ids = np.zeros(max(M_cap, 1), np.int32)
+    tok = np.zeros(max(M_cap, 1), np.int32)
+    layout = np.zeros(G + 1, np.int32)
+    st = lib().dgo_moe_route_contiguous(_ptr(e), _i64(T), _i64(G), _ptr(row), _ptr(ids), _ptr(tok),
+                                        _ptr(layout), _i64(M_cap))
+    if st != 0:
+        raise ValueError("M_cap too small for this routing")
+    return row, ids[:M_cap], tok[:M_cap], layout
+
+
+def moe_unpermute(d_bits, row_of_token):
+    """``out[t] = d[row_of_token[t]]`` (bf16 bits, u16); out-of-range rows give zeros."""
+    d = np.ascontiguousarray(d_bits, dtype=np.uint16)
+    r = np.ascontiguousarray(row_of_token, dtype=np.int32)
+    rows, N = d.shape
+    T = r.shape[0]
+    out = np.zeros((T, N), np.uint16)
+    lib().dgo_moe_unpermute(_ptr(d), _i64(N), _i64(rows), _ptr(r), _i64(T), _i64(N), _ptr(out), _i64(N))
+    return out
 
 
 def _strided(s: np.ndarray):

@@ -41,6 +41,7 @@
  */
 #include <math.h>
 #include <stdint.h>
+#include <stdlib.h>
 #include <string.h>
 
 #ifdef _OPENMP
@@ -379,4 +380,77 @@ void dgo_quantize_1x128(const void *X, int is_bf16, int64_t ldx, int64_t M, int6
             }
             S[m * s_m + kb * s_kb] = s;
         }
+}
+
+/* ------------------------------------------------------------------------
+ * MoE routing into the contiguous layout, and the way back.
+ *
+ * Tokens are grouped by expert and laid out one expert after another
+ * (regrouping tokens by expert: lpnh.cn article, §5.3), each expert's rows
+ * padded to a multiple of 128 so that every aligned 128-row block belongs to
+ * one expert (padding to aligned shapes: bhfrc.com article, §4.2), with the
+ * group id of every row and the token offsets passed on to the GEMM
+ * (rkmt.cn walkthrough, §5.3).
+ *
+ * Readings: experts in ascending id order, tokens in ascending index order
+ * inside an expert; padding rows carry id -1 and token -1; a token whose
+ * expert is outside [0, G) is dropped (row -1); rows from the end of the
+ * last segment up to M_cap are padding.
+ * ------------------------------------------------------------------------ */
+
+/* layout[e] = first row of expert e, layout[G] = rows used (M_total).
+ * Returns 0, or -1 when M_cap is too small for the routing. */
+int dgo_moe_route_contiguous(const int32_t *expert_of_token, int64_t T, int64_t G,
+                             int32_t *row_of_token, int32_t *expert_ids, int32_t *token_of_row,
+                             int32_t *layout, int64_t M_cap)
+{
+    int64_t *count = (int64_t *)calloc((size_t)(G > 0 ? G : 1), sizeof(int64_t));
+    int64_t *next = (int64_t *)calloc((size_t)(G > 0 ? G : 1), sizeof(int64_t));
+    for (int64_t t = 0; t < T; ++t) {
+        int64_t e = expert_of_token[t];
+        if (e >= 0 && e < G)
+            count[e] += 1;
+    }
+    int64_t row = 0;
+    for (int64_t e = 0; e < G; ++e) {
+        layout[e] = (int32_t)row;
+        next[e] = row;
+        row += (count[e] + BLK - 1) / BLK * BLK;
+    }
+    layout[G] = (int32_t)row;
+    if (row > M_cap) {
+        free(count);
+        free(next);
+        return -1;
+    }
+    for (int64_t r = 0; r < M_cap; ++r) {
+        expert_ids[r] = -1;
+        token_of_row[r] = -1;
+    }
+    for (int64_t t = 0; t < T; ++t) {
+        int64_t e = expert_of_token[t];
+        if (e < 0 || e >= G) {
+            row_of_token[t] = -1;
+            continue;
+        }
+        int64_t r = next[e]++;
+        row_of_token[t] = (int32_t)r;
+        expert_ids[r] = (int32_t)e;
+        token_of_row[r] = (int32_t)t;
+    }
+    free(count);
+    free(next);
+    return 0;
+}
+
+/* out[t, :] = D[row_of_token[t], :] (bf16 bits); a row index outside
+ * [0, d_rows) gives a row of zeros. */
+void dgo_moe_unpermute(const uint16_t *D, int64_t ldd, int64_t d_rows, const int32_t *row_of_token,
+                       int64_t T, int64_t N, uint16_t *out, int64_t ldo)
+{
+    for (int64_t t = 0; t < T; ++t) {
+        int64_t r = row_of_token[t];
+        for (int64_t n = 0; n < N; ++n)
+            out[t * ldo + n] = (r >= 0 && r < d_rows) ? D[r * ldd + n] : 0;
+    }
 }
