@@ -8,7 +8,9 @@ B from HBM; its metric is HBM GB/s of algorithmic bytes (A + sA + B + sB + D,
 each counted once). The other workloads are timed the same way and reported
 under "workloads", together with the 1x128 activation quantiser that
 produces the GEMM's LHS (fp32 and bf16 token activations, 8192 x 7168;
-HBM GB/s of algorithmic bytes: input + codes + scales).
+HBM GB/s of algorithmic bytes: input + codes + scales), and the whole
+contiguous MoE step (routing, quantisation into the padded layout, grouped
+GEMM, rows back in token order) on the contiguous workload's shape.
 
 Memory-bound workloads rotate over enough copies of their operands (> 2x the
 256 MB last-level cache) that every launch reads its B from HBM.
@@ -213,6 +215,87 @@ def time_quant(name, steps, warmup):
             "traffic": load_traffic(name, QUANT_SOURCES), "input_copies": n}
 
 
+MOE_LAYER = "moe_layer_g8_t8192"
+
+
+def time_moe_layer(steps, warmup):
+    """The contiguous MoE step end to end on the contiguous workload's shape
+    (8 experts, 8192 tokens, K 7168, N 4096, top-1 routing seed): routing ->
+    bf16 activations quantised into the padded layout -> grouped GEMM over
+    the layout's capacity -> rows back in token order. Whole step timed as one
+    graph of `steps` repetitions; each stage also timed on its own."""
+    import torch
+    from fp8_block_scaled_sa_amd import ops
+    from synth import gen
+    c = gen.CONFIGS["moe_contiguous_g8_t8192"]
+    G, T, N, K = c["G"], c["tokens"], c["N"], c["K"]
+    x = torch.from_numpy(gen.normal_with_outliers(np.random.Generator(np.random.PCG64(921)), (T, K)))
+    x = x.to(torch.bfloat16).cuda()
+    e = np.random.Generator(np.random.PCG64(c["seeds"][2])).choice(G, T).astype(np.int32)
+    ed = torch.from_numpy(e).cuda()
+    b, sb = gen.make_grouped_rhs(G, N, K, c["seeds"][1])
+    bd, sbd = torch.from_numpy(b).cuda(), torch.from_numpy(sb).cuda()
+    del b
+    n = max(1, min(4, -(-ROTATE_BYTES // (bd.numel() + x.numel() * 2))))
+    xs = [x] + [x.clone() for _ in range(n - 1)]
+    bs = [bd] + [bd.clone() for _ in range(n - 1)]
+    M_cap = ops.dg_moe_contiguous_max_rows(T, G)
+    row = torch.empty(T, dtype=torch.int32, device="cuda")
+    ids = torch.empty(M_cap, dtype=torch.int32, device="cuda")
+    tok = torch.empty(M_cap, dtype=torch.int32, device="cuda")
+    layout = torch.empty(G + 1, dtype=torch.int32, device="cuda")
+    q = torch.empty((M_cap, K), dtype=torch.uint8, device="cuda")
+    s = torch.empty((K // 128, M_cap), dtype=torch.float32, device="cuda").t()
+    d = torch.empty((M_cap, N), dtype=torch.bfloat16, device="cuda")
+    out = torch.empty((T, N), dtype=torch.bfloat16, device="cuda")
+    lib = ops._lib.load()
+
+    def route(i):
+        lib.dg_moe_route_contiguous(ed.data_ptr(), T, G, row.data_ptr(), ids.data_ptr(), tok.data_ptr(),
+                                    layout.data_ptr(), M_cap, torch.cuda.current_stream().cuda_stream)
+
+    def quant(i):
+        ops.dg_fp8_quantize_1x128_gather(xs[i % n], tok, q=q, s=s)
+
+    def gemm(i):
+        ops.dg_fp8_grouped_gemm_contiguous(q, s, bs[i % n], sbd, ids, d=d)
+
+    def unperm(i):
+        ops.dg_moe_unpermute(d, row, out=out)
+
+    def step(i):
+        route(i), quant(i), gemm(i), unperm(i)
+
+    def graph_us(fn):
+        for i in range(warmup):
+            fn(i)
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        cap = torch.cuda.Stream()
+        cap.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.graph(graph, stream=cap):
+            for i in range(steps):
+                fn(i)
+        graph.replay()
+        torch.cuda.synchronize()
+        a, z = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(cap)
+        with torch.cuda.stream(cap):
+            graph.replay()
+        z.record(cap)
+        torch.cuda.synchronize()
+        del graph
+        return a.elapsed_time(z) * 1e3 / steps
+
+    total = graph_us(step)
+    stages = {k: round(graph_us(f), 2) for k, f in (("route", route), ("quantize_gather", quant),
+                                                    ("grouped_gemm", gemm), ("unpermute", unperm))}
+    flops = 2 * T * N * K
+    return {"us_per_step": round(total, 2), "tflops": round(flops / total / 1e6, 1),
+            "frac_fp8_peak": round(flops / total / 1e6 / FP8_PEAK_TFLOPS, 4), "stages_us": stages,
+            "rows_used": int(layout[G].item()), "rows_capacity": M_cap, "operand_copies": n}
+
+
 def cpu_baseline(name, p, byts, min_seconds=10.0):
     """The oracle, as it stands, on this host's cores: full passes over the
     workload, repeated until at least min_seconds of work have run (one pass if
@@ -293,9 +376,13 @@ def main():
 
     others = {}
     names = [] if args.others == "none" else (
-        [n for n in list(gen.CONFIGS) + list(gen.QUANT_CONFIGS) if n != args.workload]
+        [n for n in list(gen.CONFIGS) + list(gen.QUANT_CONFIGS) + [MOE_LAYER] if n != args.workload]
         if args.others == "all" else args.others.split(","))
     for n in names:
+        if n == MOE_LAYER:
+            others[n] = time_moe_layer(max(10, args.steps // 10), max(3, args.warmup // 4))
+            torch.cuda.empty_cache()
+            continue
         if n in gen.QUANT_CONFIGS:
             # at least 50 timed launches: the graph's launch latency is spread over them
             others[n] = time_quant(n, max(50, args.steps // 4), max(3, args.warmup // 4))

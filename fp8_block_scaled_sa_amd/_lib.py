@@ -24,6 +24,11 @@ SIGNATURES = {
                                                   _p, _i64, _i64, _i64, _i64, _i64, _i64, _p]),
     "dg_fp8_quantize_1x128": (ctypes.c_int, [_p, ctypes.c_int, _i64, _p, _i64, _p, _i64, _i64,
                                              _i64, _i64, _p]),
+    "dg_fp8_quantize_1x128_gather": (ctypes.c_int, [_p, ctypes.c_int, _i64, _i64, _p, _p, _i64, _p, _i64,
+                                                    _i64, _i64, _i64, _p]),
+    "dg_moe_route_contiguous": (ctypes.c_int, [_p, _i64, _i64, _p, _p, _p, _p, _i64, _p]),
+    "dg_moe_contiguous_max_rows": (ctypes.c_int64, [_i64, _i64]),
+    "dg_moe_unpermute": (ctypes.c_int, [_p, _i64, _i64, _p, _i64, _i64, _p, _i64, _p]),
 }
 
 _lib = None

@@ -12,6 +12,7 @@
 
 #include "dg_fp8.h"
 #include "kernels.hpp"
+#include "moe.hpp"
 #include "quant.hpp"
 
 namespace {
@@ -385,6 +386,75 @@ int launch_decode(dgk::Params &p, hipStream_t stream, bool fallback)
     return e == hipSuccess ? DG_OK : fail_hip(e);
 }
 
+// The quantiser; src_rows (optional) names the row of X that each output row
+// reads (a gathered layout), x_rows the rows of X.
+int quantize_impl(const void *X, int x_dtype, int64_t ldx, int64_t x_rows, const int32_t *src_rows, void *Q,
+                  int64_t ldq, float *S, int64_t s_stride_m, int64_t s_stride_kb, int64_t M, int64_t K,
+                  void *stream)
+{
+    if (M < 0 || K <= 0 || K % 128 != 0)
+        return DG_ERR_BAD_SHAPE;
+    if (x_dtype != DG_DTYPE_F32 && x_dtype != DG_DTYPE_BF16)
+        return DG_ERR_UNSUPPORTED;
+    if (M > kInt32Max || K > kInt32Max)
+        return DG_ERR_UNSUPPORTED;
+    if (M == 0)
+        return DG_OK;
+    if ((x_rows > 0 && !X) || !Q || !S)
+        return DG_ERR_NULL_POINTER;
+    const int64_t nkb = K / 128;
+    // Every (m, kb) must own its scale: a row-major-like or an M-major-like
+    // layout (a dimension of extent 1 may take any stride).
+    const bool rows_distinct = M == 1 || s_stride_m >= 1;
+    const bool blocks_distinct = nkb == 1 || s_stride_kb >= 1;
+    const bool row_major = s_stride_m >= (nkb - 1) * s_stride_kb + 1 || M == 1;
+    const bool m_major = s_stride_kb >= (M - 1) * s_stride_m + 1 || nkb == 1;
+    if (ldx < K || ldq < K || s_stride_m < 0 || s_stride_kb < 0 || !rows_distinct || !blocks_distinct ||
+        !(row_major || m_major))
+        return DG_ERR_BAD_STRIDE;
+    const int64_t esize = x_dtype == DG_DTYPE_F32 ? 4 : 2;
+    if (!aligned(X, 16) || !aligned(Q, 16) || (ldx * esize) % 16 || ldq % 16 || !aligned(S, 4))
+        return DG_ERR_MISALIGNED;
+    const Extent eq = extent(Q, 1, (M - 1) * ldq + K - 1);
+    const Extent es = extent(S, 4, last_scale_index(M, nkb, s_stride_m, s_stride_kb));
+    if (overlaps(eq, es))
+        return DG_ERR_ALIASING;
+    if (x_rows > 0) {
+        const Extent ex = extent(X, esize, (x_rows - 1) * ldx + K - 1);
+        if (overlaps(eq, ex) || overlaps(es, ex))
+            return DG_ERR_ALIASING;
+    }
+    if (src_rows) {
+        const Extent ei = extent(src_rows, 4, M - 1);
+        if (overlaps(eq, ei) || overlaps(es, ei))
+            return DG_ERR_ALIASING;
+    }
+    const int64_t span_len = 1024 * (x_dtype == DG_DTYPE_BF16 ? dgq::groups_per_wave<true>()
+                                                             : dgq::groups_per_wave<false>());
+    const int64_t spans = (K + span_len - 1) / span_len;
+    const int64_t units = M * spans;
+    const int64_t groups = (units + dgq::kWavesPerGroup - 1) / dgq::kWavesPerGroup;
+    if (groups > kInt32Max)
+        return DG_ERR_UNSUPPORTED;
+    DeviceInfo dev;
+    int st = current_device(dev);
+    if (st != DG_OK)
+        return st;
+
+    dgq::QuantParams p = {};
+    p.X = X; p.ldx = ldx; p.src_rows = src_rows; p.x_rows = x_rows;
+    p.Q = (uint8_t *)Q; p.ldq = ldq;
+    p.S = S; p.s_m = s_stride_m; p.s_kb = s_stride_kb;
+    p.M = (int)M; p.K = (int)K; p.spans = (int)spans; p.units = units;
+    const dim3 grid((unsigned)groups), block(64 * dgq::kWavesPerGroup);
+    if (x_dtype == DG_DTYPE_BF16)
+        hipLaunchKernelGGL(dgq::quantize_1x128_kernel<true>, grid, block, 0, (hipStream_t)stream, p);
+    else
+        hipLaunchKernelGGL(dgq::quantize_1x128_kernel<false>, grid, block, 0, (hipStream_t)stream, p);
+    const hipError_t e = hipGetLastError();
+    return e == hipSuccess ? DG_OK : fail_hip(e);
+}
+
 }  // namespace
 
 extern "C" {
@@ -588,56 +658,100 @@ int dg_fp8_grouped_gemm_masked(const void *A, int64_t lda, int64_t a_stride_g, c
 int dg_fp8_quantize_1x128(const void *X, int x_dtype, int64_t ldx, void *Q, int64_t ldq, float *S,
                           int64_t s_stride_m, int64_t s_stride_kb, int64_t M, int64_t K, void *stream)
 {
-    if (M < 0 || K <= 0 || K % 128 != 0)
+    return quantize_impl(X, x_dtype, ldx, M, nullptr, Q, ldq, S, s_stride_m, s_stride_kb, M, K, stream);
+}
+
+int dg_fp8_quantize_1x128_gather(const void *X, int x_dtype, int64_t ldx, int64_t x_rows,
+                                 const int32_t *src_rows, void *Q, int64_t ldq, float *S, int64_t s_stride_m,
+                                 int64_t s_stride_kb, int64_t M, int64_t K, void *stream)
+{
+    if (x_rows < 0)
         return DG_ERR_BAD_SHAPE;
-    if (x_dtype != DG_DTYPE_F32 && x_dtype != DG_DTYPE_BF16)
-        return DG_ERR_UNSUPPORTED;
-    if (M > kInt32Max || K > kInt32Max)
-        return DG_ERR_UNSUPPORTED;
-    if (M == 0)
-        return DG_OK;
-    if (!X || !Q || !S)
+    if (M > 0 && !src_rows)
         return DG_ERR_NULL_POINTER;
-    const int64_t nkb = K / 128;
-    // Every (m, kb) must own its scale: a row-major-like or an M-major-like
-    // layout (a dimension of extent 1 may take any stride).
-    const bool rows_distinct = M == 1 || s_stride_m >= 1;
-    const bool blocks_distinct = nkb == 1 || s_stride_kb >= 1;
-    const bool row_major = s_stride_m >= (nkb - 1) * s_stride_kb + 1 || M == 1;
-    const bool m_major = s_stride_kb >= (M - 1) * s_stride_m + 1 || nkb == 1;
-    if (ldx < K || ldq < K || s_stride_m < 0 || s_stride_kb < 0 || !rows_distinct || !blocks_distinct ||
-        !(row_major || m_major))
-        return DG_ERR_BAD_STRIDE;
-    const int64_t esize = x_dtype == DG_DTYPE_F32 ? 4 : 2;
-    if (!aligned(X, 16) || !aligned(Q, 16) || (ldx * esize) % 16 || ldq % 16 || !aligned(S, 4))
+    if (src_rows && !aligned(src_rows, 4))
         return DG_ERR_MISALIGNED;
-    const Extent ex = extent(X, esize, (M - 1) * ldx + K - 1);
-    const Extent eq = extent(Q, 1, (M - 1) * ldq + K - 1);
-    const Extent es = extent(S, 4, last_scale_index(M, nkb, s_stride_m, s_stride_kb));
-    if (overlaps(eq, ex) || overlaps(es, ex) || overlaps(eq, es))
-        return DG_ERR_ALIASING;
-    const int64_t span_len = 1024 * (x_dtype == DG_DTYPE_BF16 ? dgq::groups_per_wave<true>()
-                                                             : dgq::groups_per_wave<false>());
-    const int64_t spans = (K + span_len - 1) / span_len;
-    const int64_t units = M * spans;
-    const int64_t groups = (units + dgq::kWavesPerGroup - 1) / dgq::kWavesPerGroup;
-    if (groups > kInt32Max)
+    return quantize_impl(X, x_dtype, ldx, x_rows, src_rows, Q, ldq, S, s_stride_m, s_stride_kb, M, K, stream);
+}
+
+int64_t dg_moe_contiguous_max_rows(int64_t T, int64_t G)
+{
+    if (T < 0 || G < 0)
+        return -1;
+    return 128 * ((T + 127) / 128 + std::min(G, T));
+}
+
+int dg_moe_route_contiguous(const int32_t *expert_of_token, int64_t T, int64_t G, int32_t *row_of_token,
+                            int32_t *expert_ids, int32_t *token_of_row, int32_t *layout, int64_t M_cap,
+                            void *stream)
+{
+    if (T < 0 || G <= 0 || M_cap < 0 || M_cap % 128 != 0)
+        return DG_ERR_BAD_SHAPE;
+    if (G > dgm::kMaxExperts || T > kInt32Max || M_cap > kInt32Max)
         return DG_ERR_UNSUPPORTED;
+    if (M_cap < dg_moe_contiguous_max_rows(T, G))
+        return DG_ERR_BAD_SHAPE;
+    if (!layout || (T > 0 && (!expert_of_token || !row_of_token)) || (M_cap > 0 && (!expert_ids || !token_of_row)))
+        return DG_ERR_NULL_POINTER;
+    if (!aligned(expert_of_token, 4) || !aligned(row_of_token, 4) || !aligned(expert_ids, 4) ||
+        !aligned(token_of_row, 4) || !aligned(layout, 4))
+        return DG_ERR_MISALIGNED;
+    const Extent outs[4] = {extent(row_of_token, 4, T - 1), extent(expert_ids, 4, M_cap - 1),
+                            extent(token_of_row, 4, M_cap - 1), extent(layout, 4, G)};
+    const int64_t sizes[4] = {T, M_cap, M_cap, G + 1};
+    const Extent ein = extent(expert_of_token, 4, T - 1);
+    for (int i = 0; i < 4; ++i) {
+        if (!sizes[i])
+            continue;
+        if (T > 0 && overlaps(outs[i], ein))
+            return DG_ERR_ALIASING;
+        for (int j = i + 1; j < 4; ++j)
+            if (sizes[j] && overlaps(outs[i], outs[j]))
+                return DG_ERR_ALIASING;
+    }
     DeviceInfo dev;
     int st = current_device(dev);
     if (st != DG_OK)
         return st;
+    dgm::RouteParams p = {};
+    p.expert_of_token = expert_of_token;
+    p.T = (int)T; p.G = (int)G; p.M_cap = (int)M_cap;
+    p.row_of_token = row_of_token; p.expert_ids = expert_ids; p.token_of_row = token_of_row; p.layout = layout;
+    hipLaunchKernelGGL(dgm::route_contiguous_kernel, dim3(1), dim3(dgm::kRouteThreads), 0, (hipStream_t)stream, p);
+    const hipError_t e = hipGetLastError();
+    return e == hipSuccess ? DG_OK : fail_hip(e);
+}
 
-    dgq::QuantParams p = {};
-    p.X = X; p.ldx = ldx;
-    p.Q = (uint8_t *)Q; p.ldq = ldq;
-    p.S = S; p.s_m = s_stride_m; p.s_kb = s_stride_kb;
-    p.M = (int)M; p.K = (int)K; p.spans = (int)spans; p.units = units;
-    const dim3 grid((unsigned)groups), block(64 * dgq::kWavesPerGroup);
-    if (x_dtype == DG_DTYPE_BF16)
-        hipLaunchKernelGGL(dgq::quantize_1x128_kernel<true>, grid, block, 0, (hipStream_t)stream, p);
-    else
-        hipLaunchKernelGGL(dgq::quantize_1x128_kernel<false>, grid, block, 0, (hipStream_t)stream, p);
+int dg_moe_unpermute(const void *D, int64_t ldd, int64_t d_rows, const int32_t *row_of_token, int64_t T,
+                     int64_t N, void *out, int64_t ldo, void *stream)
+{
+    if (T < 0 || N < 0 || d_rows < 0 || N % 8 != 0)
+        return DG_ERR_BAD_SHAPE;
+    if (T > kInt32Max || N > kInt32Max || d_rows > kInt32Max)
+        return DG_ERR_UNSUPPORTED;
+    if (T == 0 || N == 0)
+        return DG_OK;
+    if ((d_rows > 0 && !D) || !row_of_token || !out)
+        return DG_ERR_NULL_POINTER;
+    if (ldo < N || (d_rows > 0 && ldd < N))
+        return DG_ERR_BAD_STRIDE;
+    if (!aligned(D, 16) || !aligned(out, 16) || ldd % 8 || ldo % 8 || !aligned(row_of_token, 4))
+        return DG_ERR_MISALIGNED;
+    const Extent eo = extent(out, 2, (T - 1) * ldo + N - 1);
+    if ((d_rows > 0 && overlaps(eo, extent(D, 2, (d_rows - 1) * ldd + N - 1))) ||
+        overlaps(eo, extent(row_of_token, 4, T - 1)))
+        return DG_ERR_ALIASING;
+    DeviceInfo dev;
+    int st = current_device(dev);
+    if (st != DG_OK)
+        return st;
+    dgm::UnpermuteParams p = {};
+    p.D = (const uint16_t *)D; p.ldd = ldd; p.d_rows = (int)d_rows;
+    p.row_of_token = row_of_token; p.T = (int)T; p.N = (int)N;
+    p.out = (uint16_t *)out; p.ldo = ldo;
+    const unsigned groups = (unsigned)((T + dgm::kUnpermuteWaves - 1) / dgm::kUnpermuteWaves);
+    hipLaunchKernelGGL(dgm::unpermute_kernel, dim3(groups), dim3(64 * dgm::kUnpermuteWaves), 0,
+                       (hipStream_t)stream, p);
     const hipError_t e = hipGetLastError();
     return e == hipSuccess ? DG_OK : fail_hip(e);
 }

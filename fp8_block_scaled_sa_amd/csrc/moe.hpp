@@ -1,0 +1,196 @@
+// moe.hpp -- gfx950 kernels around the contiguous grouped GEMM: routing of
+// tokens into the padded contiguous layout, and the gather of the GEMM's rows
+// back into token order.
+//
+// Layout (regrouping tokens by expert: lpnh.cn article, §5.3; padding to
+// aligned shapes: bhfrc.com article, §4.2; group id and token offsets passed
+// to the GEMM: rkmt.cn walkthrough, §5.3): experts one after another in
+// ascending id order, each expert's tokens in ascending token order, each
+// segment padded to a multiple of 128 rows. Padding rows, and every row from
+// the last segment's end to the capacity, carry expert id -1 and token -1. A
+// token whose expert id is outside [0, G) is dropped (row -1).
+//
+// Routing is a stable counting sort in one workgroup of 16 waves. Each wave
+// owns a contiguous range of tokens, loads up to 16 chunks of 64 at once and
+// takes the chunks one after another; inside such
+// a chunk, the lanes holding one expert are found with a ballot on the first
+// remaining lane's id, so a chunk costs one round per distinct expert in it.
+// Pass 1 counts per (wave, expert); an exclusive prefix over the waves and a
+// scan over the padded segment sizes give every token's row in pass 2. No
+// atomics: the result is the same on every run.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace dgm {
+
+constexpr int kRouteWaves = 16;
+constexpr int kRouteThreads = 64 * kRouteWaves;
+constexpr int kMaxExperts = 1024;
+
+struct RouteParams {
+    const int32_t *expert_of_token;  // [T]
+    int T, G, M_cap;
+    int32_t *row_of_token;           // [T]
+    int32_t *expert_ids;             // [M_cap]
+    int32_t *token_of_row;           // [M_cap]
+    int32_t *layout;                 // [G + 1]: first row of each expert, then the rows used
+};
+
+// Chunks of 64 tokens a wave loads at once. The loads are unconditional (the
+// index is clamped into [0, T), and tokens outside the wave's range are
+// masked afterwards), so all of them are in flight before the first wait; a
+// load per chunk inside the loop cost one memory latency per chunk.
+constexpr int kChunks = 16;
+
+__device__ __forceinline__ void load_experts(const RouteParams &p, int base, int t_end, int lane, int (&e)[kChunks])
+{
+#pragma unroll
+    for (int c = 0; c < kChunks; ++c) {
+        const int t = base + 64 * c + lane;
+        const int v = p.expert_of_token[min(t, p.T - 1)];
+        e[c] = (t < t_end && v >= 0 && v < p.G) ? v : -1;
+    }
+}
+
+__global__ __launch_bounds__(kRouteThreads) void route_contiguous_kernel(RouteParams p)
+{
+    __shared__ int cnt[kRouteWaves][kMaxExperts];  // per-wave counts, then per-wave running offsets
+    __shared__ int seg[kMaxExperts + 1];           // first row of each expert's segment
+    __shared__ int tot[kMaxExperts];               // tokens per expert
+    const int lane = threadIdx.x & 63;
+    const int w = threadIdx.x >> 6;
+    for (int e = lane; e < p.G; e += 64)
+        cnt[w][e] = 0;
+    __syncthreads();
+
+    const int chunk = (p.T + kRouteWaves - 1) / kRouteWaves;
+    const int t0 = min(p.T, w * chunk), t1 = min(p.T, t0 + chunk);
+    for (int sc = t0; sc < t1; sc += 64 * kChunks) {
+        int ex[kChunks];
+        load_experts(p, sc, t1, lane, ex);
+#pragma unroll
+        for (int c = 0; c < kChunks; ++c) {
+            if (sc + 64 * c >= t1)
+                break;
+            const int e = ex[c];
+            uint64_t todo = __ballot(e >= 0);
+            while (todo) {
+                const int leader = __ffsll((unsigned long long)todo) - 1;
+                const int el = __shfl(e, leader);
+                const uint64_t same = __ballot(e == el);
+                if (lane == leader)
+                    cnt[w][el] += __popcll(same);
+                todo &= ~same;
+            }
+        }
+    }
+    __syncthreads();
+
+    const int e = threadIdx.x;  // G <= kMaxExperts == kRouteThreads: one expert per thread
+    if (e < p.G) {
+        int run = 0;
+        for (int v = 0; v < kRouteWaves; ++v) {
+            const int c = cnt[v][e];
+            cnt[v][e] = run;
+            run += c;
+        }
+        tot[e] = run;
+        seg[e + 1] = (run + 127) / 128 * 128;
+    }
+    if (threadIdx.x == 0)
+        seg[0] = 0;
+    __syncthreads();
+    for (int off = 1; off < p.G; off <<= 1) {  // inclusive scan of seg[1..G]
+        const int i = threadIdx.x + 1;
+        const int v = (i <= p.G && i - off >= 1) ? seg[i - off] : 0;
+        __syncthreads();
+        if (i <= p.G)
+            seg[i] += v;
+        __syncthreads();
+    }
+    if (threadIdx.x < p.G)
+        p.layout[threadIdx.x] = seg[threadIdx.x];
+    if (threadIdx.x == 0)
+        p.layout[p.G] = seg[p.G];
+
+    // Rows that hold no token: the tail of each expert's segment (wave w takes
+    // experts w, w + 16, ...) and everything past the last segment.
+    for (int g = w; g < p.G; g += kRouteWaves)
+        for (int r = seg[g] + tot[g] + lane; r < seg[g + 1]; r += 64) {
+            p.expert_ids[r] = -1;
+            p.token_of_row[r] = -1;
+        }
+    for (int r = seg[p.G] + threadIdx.x; r < p.M_cap; r += kRouteThreads) {
+        p.expert_ids[r] = -1;
+        p.token_of_row[r] = -1;
+    }
+
+    for (int sc = t0; sc < t1; sc += 64 * kChunks) {
+        int ex[kChunks];
+        load_experts(p, sc, t1, lane, ex);
+#pragma unroll
+        for (int c = 0; c < kChunks; ++c) {
+            if (sc + 64 * c >= t1)
+                break;
+            const int t = sc + 64 * c + lane;
+            const int e = ex[c];
+            uint64_t todo = __ballot(e >= 0);
+            int row = -1;
+            while (todo) {
+                const int leader = __ffsll((unsigned long long)todo) - 1;
+                const int el = __shfl(e, leader);
+                const uint64_t same = __ballot(e == el);
+                if (e == el)
+                    row = seg[el] + cnt[w][el] + __popcll(same & ((1ull << lane) - 1));
+                if (lane == leader)
+                    cnt[w][el] += __popcll(same);
+                todo &= ~same;
+            }
+            if (t < t1) {
+                p.row_of_token[t] = row;
+                if (row >= 0) {
+                    p.token_of_row[row] = t;
+                    p.expert_ids[row] = e;
+                }
+            }
+        }
+    }
+}
+
+struct UnpermuteParams {
+    const uint16_t *D;   // bf16 [d_rows, N], row stride ldd
+    int64_t ldd;
+    int d_rows;
+    const int32_t *row_of_token;
+    int T, N;
+    uint16_t *out;       // bf16 [T, N], row stride ldo
+    int64_t ldo;
+};
+
+typedef uint32_t u32x4m __attribute__((ext_vector_type(4)));
+constexpr int kUnpermuteWaves = 4;
+
+// out[t, :] = D[row_of_token[t], :]; a row index outside [0, d_rows) gives
+// zeros. One wave per token, 16 bytes per lane and step.
+__global__ __launch_bounds__(64 * kUnpermuteWaves) void unpermute_kernel(UnpermuteParams p)
+{
+    const int t = blockIdx.x * kUnpermuteWaves + (threadIdx.x >> 6);
+    if (t >= p.T)
+        return;
+    const int lane = threadIdx.x & 63;
+    const int r = p.row_of_token[t];
+    uint16_t *dst = p.out + (int64_t)t * p.ldo;
+    if (r < 0 || r >= p.d_rows) {
+        for (int n = 8 * lane; n < p.N; n += 512)
+            *(u32x4m *)(dst + n) = u32x4m{0, 0, 0, 0};
+        return;
+    }
+    const uint16_t *src = p.D + (int64_t)r * p.ldd;
+#pragma unroll 4
+    for (int n = 8 * lane; n < p.N; n += 512)
+        *(u32x4m *)(dst + n) = *(const u32x4m *)(src + n);
+}
+
+}  // namespace dgm

@@ -45,8 +45,10 @@
 namespace dgq {
 
 struct QuantParams {
-    const void *X;   // fp32 or bf16 [M, K], row stride ldx elements
+    const void *X;   // fp32 or bf16 [x_rows, K], row stride ldx elements
     int64_t ldx;
+    const int32_t *src_rows;  // output row r quantises X[src_rows[r]] (NULL: X[r]);
+    int64_t x_rows;           // a source row outside [0, x_rows) reads as zeros
     uint8_t *Q;      // e4m3 codes [M, K], row stride ldq bytes
     int64_t ldq;
     float *S;        // S[m, kb] at S[m * s_m + kb * s_kb]
@@ -117,6 +119,8 @@ __global__ __launch_bounds__(64 * kWavesPerGroup) void quantize_1x128_kernel(Qua
         return;
     const int row = (int)(unit / p.spans);
     const int span = (int)(unit - (int64_t)row * p.spans);
+    const int64_t src = p.src_rows ? (int64_t)p.src_rows[row] : (int64_t)row;
+    const bool present = src >= 0 && src < p.x_rows;
     const int nkb = p.K >> 7;
     const int sub = lane & 7;
     auto offset = [&](int t) { return BF16 ? 8 * sub + 64 * t : 4 * sub + 32 * t; };
@@ -125,27 +129,36 @@ __global__ __launch_bounds__(64 * kWavesPerGroup) void quantize_1x128_kernel(Qua
     // the row's last block instead, and its results are not stored), so the
     // compiler issues all of a wave's loads before the first wait.
     float x[G][NL * EL];
+    if (present) {
 #pragma unroll
-    for (int g = 0; g < G; ++g) {
-        const int kb = min(span * 8 * G + 8 * g + (lane >> 3), nkb - 1);
-        const int64_t base = (int64_t)row * p.ldx + kb * 128;
+        for (int g = 0; g < G; ++g) {
+            const int kb = min(span * 8 * G + 8 * g + (lane >> 3), nkb - 1);
+            const int64_t base = src * p.ldx + kb * 128;
 #pragma unroll
-        for (int t = 0; t < NL; ++t) {
-            if (BF16) {
-                const u32x4 v =
-                    __builtin_nontemporal_load((const u32x4 *)((const uint16_t *)p.X + base + offset(t)));
+            for (int t = 0; t < NL; ++t) {
+                if (BF16) {
+                    const u32x4 v =
+                        __builtin_nontemporal_load((const u32x4 *)((const uint16_t *)p.X + base + offset(t)));
 #pragma unroll
-                for (int c = 0; c < 4; ++c) {
-                    x[g][EL * t + 2 * c] = bf16_to_f32(v[c] & 0xffffu);
-                    x[g][EL * t + 2 * c + 1] = bf16_to_f32(v[c] >> 16);
+                    for (int c = 0; c < 4; ++c) {
+                        x[g][EL * t + 2 * c] = bf16_to_f32(v[c] & 0xffffu);
+                        x[g][EL * t + 2 * c + 1] = bf16_to_f32(v[c] >> 16);
+                    }
+                } else {
+                    const f32x4 v =
+                        __builtin_nontemporal_load((const f32x4 *)((const float *)p.X + base + offset(t)));
+#pragma unroll
+                    for (int c = 0; c < 4; ++c)
+                        x[g][EL * t + c] = v[c];
                 }
-            } else {
-                const f32x4 v = __builtin_nontemporal_load((const f32x4 *)((const float *)p.X + base + offset(t)));
-#pragma unroll
-                for (int c = 0; c < 4; ++c)
-                    x[g][EL * t + c] = v[c];
             }
         }
+    } else {  // a padding row of a gathered layout: zeros, so codes 0 and scale 1
+#pragma unroll
+        for (int g = 0; g < G; ++g)
+#pragma unroll
+            for (int c = 0; c < NL * EL; ++c)
+                x[g][c] = 0.0f;
     }
 
 #pragma unroll

@@ -162,3 +162,77 @@ def dg_fp8_quantize_1x128(x, q=None, s=None, stream=None):
                                    _dev(s, "s"), s.stride(0), s.stride(1), M, K, _stream(stream))
     _check(st, "dg_fp8_quantize_1x128")
     return q, s
+
+
+def _dev_or_null(t, name):
+    return None if t is None or t.numel() == 0 else _dev(t, name)
+
+
+def dg_fp8_quantize_1x128_gather(x, src_rows, q=None, s=None, stream=None):
+    """Quantise rows x[src_rows[r]] into Q[r] (a source index outside
+    [0, x.shape[0]) gives a zero row: codes 0, scale 1). Returns (q, s) with
+    s M-major as in dg_fp8_quantize_1x128."""
+    if x.dtype not in DTYPES:
+        raise TypeError("x must be float32 or bfloat16")
+    if x.dim() != 2 or x.stride(-1) != 1:
+        raise ValueError("x must be 2-D with a contiguous last (K) dimension")
+    if src_rows.dtype != torch.int32 or src_rows.dim() != 1:
+        raise TypeError("src_rows must be a 1-D int32 tensor")
+    M, K = src_rows.shape[0], x.shape[1]
+    if q is None:
+        q = torch.empty((M, K), dtype=torch.uint8, device=x.device)
+    if s is None:
+        s = torch.empty((K // BLOCK, M), dtype=torch.float32, device=x.device).t()
+    _codes(q, "q", 2), _scales(s, "s", 2)
+    if tuple(q.shape) != (M, K) or tuple(s.shape) != (M, K // BLOCK):
+        raise ValueError("shape mismatch")
+    lib = _lib.load()
+    st = lib.dg_fp8_quantize_1x128_gather(_dev_or_null(x, "x"), DTYPES[x.dtype], x.stride(0), x.shape[0],
+                                          _dev_or_null(src_rows, "src_rows"), _dev(q, "q"), q.stride(0),
+                                          _dev(s, "s"), s.stride(0), s.stride(1), M, K, _stream(stream))
+    _check(st, "dg_fp8_quantize_1x128_gather")
+    return q, s
+
+
+def dg_moe_contiguous_max_rows(T: int, G: int) -> int:
+    return int(_lib.load().dg_moe_contiguous_max_rows(T, G))
+
+
+def dg_moe_route_contiguous(expert_of_token, G, M_cap=None, stream=None):
+    """Routing of top-1 tokens into the contiguous layout. Returns
+    (row_of_token [T], expert_ids [M_cap], token_of_row [M_cap], layout [G+1]),
+    all int32 device tensors; M_cap defaults to the worst case."""
+    if expert_of_token.dtype != torch.int32 or expert_of_token.dim() != 1:
+        raise TypeError("expert_of_token must be a 1-D int32 tensor")
+    T = expert_of_token.shape[0]
+    dev = expert_of_token.device
+    M_cap = dg_moe_contiguous_max_rows(T, G) if M_cap is None else M_cap
+    row = torch.empty(T, dtype=torch.int32, device=dev)
+    ids = torch.empty(M_cap, dtype=torch.int32, device=dev)
+    tok = torch.empty(M_cap, dtype=torch.int32, device=dev)
+    layout = torch.empty(G + 1, dtype=torch.int32, device=dev)
+    lib = _lib.load()
+    st = lib.dg_moe_route_contiguous(_dev_or_null(expert_of_token, "expert_of_token"), T, G,
+                                     _dev_or_null(row, "row"), _dev_or_null(ids, "ids"),
+                                     _dev_or_null(tok, "tok"), _dev(layout, "layout"), M_cap, _stream(stream))
+    _check(st, "dg_moe_route_contiguous")
+    return row, ids, tok, layout
+
+
+def dg_moe_unpermute(d, row_of_token, out=None, stream=None):
+    """out[t] = d[row_of_token[t]] (bf16 rows); out-of-range rows give zeros."""
+    if d.dtype != torch.bfloat16 or d.dim() != 2 or d.stride(-1) != 1:
+        raise TypeError("d must be a 2-D bfloat16 tensor with contiguous rows")
+    if row_of_token.dtype != torch.int32 or row_of_token.dim() != 1:
+        raise TypeError("row_of_token must be a 1-D int32 tensor")
+    T, N = row_of_token.shape[0], d.shape[1]
+    if out is None:
+        out = torch.empty((T, N), dtype=torch.bfloat16, device=d.device)
+    if out.dtype != torch.bfloat16 or tuple(out.shape) != (T, N) or out.stride(-1) != 1:
+        raise ValueError("out must be a bfloat16 [T, N] tensor with contiguous rows")
+    lib = _lib.load()
+    st = lib.dg_moe_unpermute(_dev_or_null(d, "d"), d.stride(0), d.shape[0],
+                              _dev_or_null(row_of_token, "row_of_token"), T, N,
+                              _dev_or_null(out, "out"), out.stride(0), _stream(stream))
+    _check(st, "dg_moe_unpermute")
+    return out

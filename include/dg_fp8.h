@@ -21,7 +21,10 @@
  * "NT": A is [M, K] and B is [N, K], both with K contiguous, D = A . B^T.
  *
  * dg_fp8_quantize_1x128 (at the end) produces A and sA from fp32 or bf16
- * activations: the quantisation step that precedes the GEMM.
+ * activations: the quantisation step that precedes the GEMM. For the
+ * contiguous MoE layout, dg_moe_route_contiguous lays tokens out by expert,
+ * dg_fp8_quantize_1x128_gather quantises them into that layout and
+ * dg_moe_unpermute brings the GEMM's rows back into token order.
  *
  * Conventions shared by every entry point
  *   - All pointers are DEVICE pointers owned by the caller; the library never
@@ -198,6 +201,63 @@ int dg_fp8_quantize_1x128(const void *X, int x_dtype, int64_t ldx,
                           void *Q, int64_t ldq,
                           float *S, int64_t s_stride_m, int64_t s_stride_kb,
                           int64_t M, int64_t K, void *stream);
+
+/*
+ * The quantiser over a gathered row order: output row r quantises row
+ * src_rows[r] of X (device memory, int32 [M]); a source index outside
+ * [0, x_rows) reads as a row of zeros, which gives codes 0 and scale 1 (the
+ * padding rows of the contiguous MoE layout). With src_rows = token_of_row of
+ * dg_moe_route_contiguous this quantises token activations straight into the
+ * contiguous layout in one pass.
+ *   X  [x_rows, K] fp32/bf16, row stride ldx;  Q, S as in dg_fp8_quantize_1x128, M output rows.
+ * Errors as dg_fp8_quantize_1x128; also DG_ERR_NULL_POINTER for a NULL
+ * src_rows when M > 0, DG_ERR_BAD_SHAPE for x_rows < 0.
+ */
+int dg_fp8_quantize_1x128_gather(const void *X, int x_dtype, int64_t ldx, int64_t x_rows,
+                                 const int32_t *src_rows,
+                                 void *Q, int64_t ldq,
+                                 float *S, int64_t s_stride_m, int64_t s_stride_kb,
+                                 int64_t M, int64_t K, void *stream);
+
+/*
+ * MoE routing into the contiguous layout that dg_fp8_grouped_gemm_contiguous
+ * takes: tokens regrouped by expert (lpnh.cn article, §5.3), each expert's
+ * rows padded to a multiple of 128 (bhfrc.com article, §4.2), with the group
+ * id and source token of every row (rkmt.cn walkthrough, §5.3).
+ *   expert_of_token [T] int32 (device): top-1 expert of each token
+ *   row_of_token    [T] int32 (written): the token's row, -1 if dropped
+ *   expert_ids      [M_cap] int32 (written): expert of each row, -1 for padding
+ *   token_of_row    [M_cap] int32 (written): source token of each row, -1 for padding
+ *   layout          [G + 1] int32 (written): first row of each expert; layout[G] = rows used
+ * Experts are laid out in ascending id order, tokens in ascending order
+ * within an expert. A token whose id is outside [0, G) is dropped. Rows from
+ * layout[G] to M_cap are padding, so the GEMM may run over all M_cap rows
+ * (its blocks of padding rows are skipped) without reading layout[G] on the
+ * host. Everything stays on the device: no synchronisation, capture-safe.
+ * Deterministic (no atomics). One workgroup.
+ * Constraints: 1 <= G <= 1024; M_cap % 128 == 0 and
+ * M_cap >= dg_moe_contiguous_max_rows(T, G) (else DG_ERR_BAD_SHAPE); all
+ * arrays 4-byte aligned and pairwise disjoint.
+ */
+int dg_moe_route_contiguous(const int32_t *expert_of_token, int64_t T, int64_t G,
+                            int32_t *row_of_token, int32_t *expert_ids, int32_t *token_of_row,
+                            int32_t *layout, int64_t M_cap, void *stream);
+
+/* Rows that always hold the padded layout of T tokens over G experts:
+ * 128 * (ceil(T / 128) + min(G, T)). -1 for negative arguments. */
+int64_t dg_moe_contiguous_max_rows(int64_t T, int64_t G);
+
+/*
+ * The way back from the contiguous layout: out[t, :] = D[row_of_token[t], :]
+ * (bf16, bit copy), for t < T; a row index outside [0, d_rows) (a dropped
+ * token) gives a row of zeros.
+ *   D [d_rows, N] bf16, row stride ldd;  out [T, N] bf16, row stride ldo (written)
+ * Constraints: N % 8 == 0; D and out 16-byte aligned, ldd and ldo multiples
+ * of 8; out disjoint from D and row_of_token.
+ */
+int dg_moe_unpermute(const void *D, int64_t ldd, int64_t d_rows,
+                     const int32_t *row_of_token, int64_t T, int64_t N,
+                     void *out, int64_t ldo, void *stream);
 
 #ifdef __cplusplus
 }

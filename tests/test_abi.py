@@ -18,7 +18,7 @@ DG_ERR_BAD_STRIDE, DG_ERR_UNSUPPORTED, DG_ERR_HIP, DG_ERR_ALIASING = 4, 5, 6, 7
 
 def declared_symbols():
     text = open(HEADER).read()
-    return sorted(set(re.findall(r"^\s*(?:int|const char \*)\s*(dg_\w+)\s*\(", text, re.M)))
+    return sorted(set(re.findall(r"^\s*(?:int|int64_t|const char \*)\s*(dg_\w+)\s*\(", text, re.M)))
 
 
 def test_header_declares_the_entry_points():
@@ -187,3 +187,82 @@ def test_quantize_accepts_both_scale_layouts_up_to_the_device_check():
 def test_quantize_empty():
     assert quant(M=0) == DG_OK
     assert quant(M=0, X=None, Q=None, S=None) == DG_OK
+
+
+def gather(**kw):
+    args = dict(X=X, x_dtype=1, ldx=512, x_rows=100, src=IDS, Q=Q, ldq=512, S=S, s_m=1, s_kb=64,
+                M=64, K=512, stream=None)
+    args.update(kw)
+    return _lib.load().dg_fp8_quantize_1x128_gather(*args.values())
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(src=None), DG_ERR_NULL_POINTER),
+    (dict(src=IDS + 2), DG_ERR_MISALIGNED),
+    (dict(x_rows=-1), DG_ERR_BAD_SHAPE),
+    (dict(src=Q + 64), DG_ERR_ALIASING),
+    (dict(K=100), DG_ERR_BAD_SHAPE),
+    (dict(X=None), DG_ERR_NULL_POINTER),
+])
+def test_gather_quantize_validation(kw, status):
+    assert gather(**kw) == status
+
+
+def test_gather_quantize_all_padding_needs_no_input():
+    assert gather(X=None, x_rows=0) in (DG_OK, DG_ERR_HIP, DG_ERR_UNSUPPORTED)
+    assert gather(M=0, src=None) == DG_OK
+
+
+E, ROW, EIDS, TOK, LAY = (0x10000000 * (i + 10) for i in range(5))
+
+
+def route(**kw):
+    args = dict(e=E, T=1000, G=8, row=ROW, ids=EIDS, tok=TOK, layout=LAY, M_cap=2048, stream=None)
+    args.update(kw)
+    return _lib.load().dg_moe_route_contiguous(*args.values())
+
+
+def test_max_rows():
+    lib = _lib.load()
+    assert lib.dg_moe_contiguous_max_rows(8192, 8) == 128 * 72
+    assert lib.dg_moe_contiguous_max_rows(5, 100) == 128 * 6
+    assert lib.dg_moe_contiguous_max_rows(0, 4) == 0
+    assert lib.dg_moe_contiguous_max_rows(-1, 4) == -1
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(G=0), DG_ERR_BAD_SHAPE),
+    (dict(T=-1), DG_ERR_BAD_SHAPE),
+    (dict(M_cap=2000), DG_ERR_BAD_SHAPE),           # not a multiple of 128
+    (dict(M_cap=1024), DG_ERR_BAD_SHAPE),           # below 128 * (ceil(T/128) + min(G, T)) = 2048
+    (dict(G=1025, M_cap=128 * 1008), DG_ERR_UNSUPPORTED),
+    (dict(e=None), DG_ERR_NULL_POINTER),
+    (dict(layout=None), DG_ERR_NULL_POINTER),
+    (dict(ids=EIDS + 2), DG_ERR_MISALIGNED),
+    (dict(tok=EIDS + 1024), DG_ERR_ALIASING),
+    (dict(row=E), DG_ERR_ALIASING),
+])
+def test_route_validation(kw, status):
+    assert route(**kw) == status
+
+
+def unperm(**kw):
+    args = dict(D=D, ldd=256, d_rows=512, row=IDS, T=300, N=256, out=A, ldo=256, stream=None)
+    args.update(kw)
+    return _lib.load().dg_moe_unpermute(*args.values())
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(N=100), DG_ERR_BAD_SHAPE),
+    (dict(row=None), DG_ERR_NULL_POINTER),
+    (dict(ldo=128), DG_ERR_BAD_STRIDE),
+    (dict(ldd=260), DG_ERR_MISALIGNED),
+    (dict(out=A + 8), DG_ERR_MISALIGNED),
+    (dict(out=D + 1024), DG_ERR_ALIASING),
+])
+def test_unpermute_validation(kw, status):
+    assert unperm(**kw) == status
+
+
+def test_unpermute_empty():
+    assert unperm(T=0) == DG_OK
