@@ -51,6 +51,12 @@ def lib():
         _lib.dgo_e4m3_encode.argtypes = [ctypes.c_float]
         _lib.dgo_quantize_1x128.restype = None
         _lib.dgo_moe_route_contiguous.restype = ctypes.c_int
+        _lib.dgo_e5m2_decode.restype = ctypes.c_double
+        _lib.dgo_e5m2_decode.argtypes = [ctypes.c_uint8]
+        _lib.dgo_block_partial_fmt.restype = ctypes.c_double
+        _lib.dgo_block_partial_fmt.argtypes = [_p, ctypes.c_int, _p, ctypes.c_int]
+        _lib.dgo_gemm_nt_fmt.restype = None
+        _lib.dgo_gemm_nt_fmt_points.restype = None
         _lib.dgo_moe_unpermute.restype = None
         for name in ("dgo_gemm_nt", "dgo_gemm_nt_points", "dgo_grouped_contiguous",
                      "dgo_grouped_contiguous_points", "dgo_grouped_masked",
@@ -240,6 +246,54 @@ def quantize_1x128(x, threads=None):
     lib().dgo_quantize_1x128(_ptr(x), ctypes.c_int(int(is_bf16)), _i64(K), _i64(M), _i64(K),
                              _ptr(q), _i64(K), _ptr(s), _i64(K // 128), _i64(1), _threads(threads))
     return q, s
+
+
+FMTS = {"e4m3": 0, "e5m2": 1}
+
+
+def e5m2_decode(code: int) -> float:
+    return float(lib().dgo_e5m2_decode(int(code)))
+
+
+def block_partial_fmt(a128, fa, b128, fb) -> float:
+    a = np.ascontiguousarray(a128, dtype=np.uint8)
+    b = np.ascontiguousarray(b128, dtype=np.uint8)
+    assert a.size == 128 and b.size == 128
+    return float(lib().dgo_block_partial_fmt(_ptr(a), ctypes.c_int(FMTS[fa]), _ptr(b), ctypes.c_int(FMTS[fb])))
+
+
+def gemm_nt_fmt(a, fa, sa, b, fb, sb, want_acc=False, threads=None):
+    """Dense NT with operand formats ``fa``/``fb`` ("e4m3" or "e5m2"); else as gemm_nt."""
+    a = np.ascontiguousarray(a, dtype=np.uint8)
+    b = np.ascontiguousarray(b, dtype=np.uint8)
+    M, K = a.shape
+    N = b.shape[0]
+    sa_base, sa_m, sa_kb = _strided(np.asarray(sa, dtype=np.float32))
+    sb_base, sb_nb, sb_kb = _strided(np.asarray(sb, dtype=np.float32))
+    d = np.zeros((M, N), dtype=np.uint16)
+    acc = np.zeros((M, N), dtype=np.float64) if want_acc else None
+    lib().dgo_gemm_nt_fmt(_ptr(a), ctypes.c_int(FMTS[fa]), _i64(K), sa_base, _i64(sa_m), _i64(sa_kb),
+                          _ptr(b), ctypes.c_int(FMTS[fb]), _i64(K), sb_base, _i64(sb_nb), _i64(sb_kb),
+                          _i64(M), _i64(N), _i64(K), _ptr(acc) if acc is not None else None, _ptr(d), _i64(N),
+                          _threads(threads))
+    return (d, acc) if want_acc else d
+
+
+def gemm_nt_fmt_points(a, fa, sa, b, fb, sb, ms, ns, threads=None):
+    a = np.ascontiguousarray(a, dtype=np.uint8)
+    b = np.ascontiguousarray(b, dtype=np.uint8)
+    K = a.shape[1]
+    sa_base, sa_m, sa_kb = _strided(np.asarray(sa, dtype=np.float32))
+    sb_base, sb_nb, sb_kb = _strided(np.asarray(sb, dtype=np.float32))
+    ms = np.ascontiguousarray(ms, dtype=np.int64)
+    ns = np.ascontiguousarray(ns, dtype=np.int64)
+    cnt = ms.shape[0]
+    acc = np.zeros(cnt, dtype=np.float64)
+    d = np.zeros(cnt, dtype=np.uint16)
+    lib().dgo_gemm_nt_fmt_points(_ptr(a), ctypes.c_int(FMTS[fa]), _i64(K), sa_base, _i64(sa_m), _i64(sa_kb),
+                                 _ptr(b), ctypes.c_int(FMTS[fb]), _i64(K), sb_base, _i64(sb_nb), _i64(sb_kb),
+                                 _i64(K), _ptr(ms), _ptr(ns), _i64(cnt), _ptr(acc), _ptr(d), _threads(threads))
+    return d, acc
 
 
 def moe_max_rows(T: int, G: int) -> int:

@@ -454,3 +454,99 @@ void dgo_moe_unpermute(const uint16_t *D, int64_t ldd, int64_t d_rows, const int
             out[t * ldo + n] = (r >= 0 && r < d_rows) ? D[r * ldd + n] : 0;
     }
 }
+
+/* ------------------------------------------------------------------------
+ * e5m2 operands. Each operand of the GEMM may instead hold e5m2 codes: 1
+ * sign, 5 exponent bits (bias 15), 2 mantissa bits, largest finite 57344,
+ * S.11111.00 infinity and S.11111.xx NaN (the two fp8 formats: rkmt.cn
+ * walkthrough §2.1; A in e4m3 with B in e5m2 trades precision for range:
+ * lpnh.cn article §2.1). The operation is unchanged; a block's scale of an
+ * e5m2 operand is amax / 57344.
+ *
+ * Precision. An e5m2 value is an integer multiple of 2^-16 below 2^16, so a
+ * product with e5m2 in it can need up to 64 bits and a 128-term block sum no
+ * longer fits binary64. The block sum is therefore taken exactly in 128-bit
+ * integers (value * 2^9 for e4m3, value * 2^16 for e5m2) and converted to
+ * binary64 once.
+ * ------------------------------------------------------------------------ */
+
+double dgo_e5m2_decode(uint8_t code)
+{
+    int s = (code >> 7) & 1;
+    int e = (code >> 2) & 31;
+    int f = code & 3;
+    double mag;
+    if (e == 31)
+        return f ? NAN : (s ? -INFINITY : INFINITY);
+    if (e == 0)
+        mag = ldexp((double)f, -16);            /* subnormal: f/4 * 2^-14 */
+    else
+        mag = ldexp((double)(4 + f), e - 17);   /* (1 + f/4) * 2^(e-15) */
+    return s ? -mag : mag;
+}
+
+/* fmt 0: e4m3, fmt 1: e5m2. Integer value of a code times 2^(9 or 16). */
+static int64_t code_int(uint8_t code, int fmt)
+{
+    double v = fmt ? dgo_e5m2_decode(code) : dgo_e4m3_decode(code);
+    return (int64_t)ldexp(v, fmt ? 16 : 9);     /* exact: the value is a multiple of 2^-16 or 2^-9 */
+}
+
+static int code_shift(int fmt) { return fmt ? 16 : 9; }
+
+/* Block partial for formats (fa, fb): exact 128-bit integer sum, one rounding to binary64. */
+double dgo_block_partial_fmt(const uint8_t *a, int fa, const uint8_t *b, int fb)
+{
+    __int128 acc = 0;
+    for (int k = 0; k < BLK; ++k)
+        acc += (__int128)code_int(a[k], fa) * (__int128)code_int(b[k], fb);
+    return ldexp((double)acc, -(code_shift(fa) + code_shift(fb)));
+}
+
+static double element_fmt(const uint8_t *a, int fa, const float *sa, int64_t sa_kb,
+                          const uint8_t *b, int fb, const float *sb, int64_t sb_kb, int64_t K)
+{
+    double acc = 0.0;
+    for (int64_t kb = 0; kb < K / BLK; ++kb) {
+        double partial = dgo_block_partial_fmt(a + kb * BLK, fa, b + kb * BLK, fb);
+        double scale = (double)sa[kb * sa_kb] * (double)sb[kb * sb_kb];
+        acc += partial * scale;
+    }
+    return acc;
+}
+
+/* Dense NT with operand formats fa (A) and fb (B); otherwise as dgo_gemm_nt. */
+void dgo_gemm_nt_fmt(const uint8_t *A, int fa, int64_t lda, const float *sA, int64_t sa_m, int64_t sa_kb,
+                     const uint8_t *B, int fb, int64_t ldb, const float *sB, int64_t sb_nb, int64_t sb_kb,
+                     int64_t M, int64_t N, int64_t K, double *acc, uint16_t *D, int64_t ldd, int threads)
+{
+    init_table();
+    set_threads(threads);
+#pragma omp parallel for collapse(2) schedule(static)
+    for (int64_t m = 0; m < M; ++m)
+        for (int64_t n = 0; n < N; ++n) {
+            double v = element_fmt(A + m * lda, fa, sA + m * sa_m, sa_kb,
+                                   B + n * ldb, fb, sB + (n / BLK) * sb_nb, sb_kb, K);
+            if (acc)
+                acc[m * N + n] = v;
+            D[m * ldd + n] = dgo_bf16_rne(v);
+        }
+}
+
+/* Dense NT with operand formats at chosen output points (ms[i], ns[i]). */
+void dgo_gemm_nt_fmt_points(const uint8_t *A, int fa, int64_t lda, const float *sA, int64_t sa_m, int64_t sa_kb,
+                            const uint8_t *B, int fb, int64_t ldb, const float *sB, int64_t sb_nb, int64_t sb_kb,
+                            int64_t K, const int64_t *ms, const int64_t *ns, int64_t count,
+                            double *acc, uint16_t *d, int threads)
+{
+    init_table();
+    set_threads(threads);
+#pragma omp parallel for schedule(static)
+    for (int64_t i = 0; i < count; ++i) {
+        double v = element_fmt(A + ms[i] * lda, fa, sA + ms[i] * sa_m, sa_kb,
+                               B + ns[i] * ldb, fb, sB + (ns[i] / BLK) * sb_nb, sb_kb, K);
+        if (acc)
+            acc[i] = v;
+        d[i] = dgo_bf16_rne(v);
+    }
+}

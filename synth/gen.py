@@ -40,6 +40,9 @@ import numpy as np
 import torch
 
 E4M3_MAX = 448.0
+E5M2_MAX = 57344.0
+# operand formats: largest finite value and torch dtype of the encoder
+FORMATS = {"e4m3": (E4M3_MAX, torch.float8_e4m3fn), "e5m2": (E5M2_MAX, torch.float8_e5m2)}
 BLOCK = 128
 OUTLIER_P = 1e-3
 OUTLIER_MUL = 50.0
@@ -54,17 +57,18 @@ def normal_with_outliers(rng: np.random.Generator, shape) -> np.ndarray:
     return x
 
 
-def _encode(q: torch.Tensor) -> torch.Tensor:
-    q = torch.clamp(q, -E4M3_MAX, E4M3_MAX)
-    return q.to(torch.float8_e4m3fn).view(torch.uint8)
+def _encode(q: torch.Tensor, fmt: str = "e4m3") -> torch.Tensor:
+    fmax, dtype = FORMATS[fmt]
+    q = torch.clamp(q, -fmax, fmax)
+    return q.to(dtype).view(torch.uint8)
 
 
-def _block_scale(amax: torch.Tensor) -> torch.Tensor:
-    s = amax / torch.tensor(E4M3_MAX, dtype=torch.float32)
+def _block_scale(amax: torch.Tensor, fmt: str = "e4m3") -> torch.Tensor:
+    s = amax / torch.tensor(FORMATS[fmt][0], dtype=torch.float32)
     return torch.where(amax == 0, torch.ones_like(s), s)
 
 
-def quantize_lhs(x: np.ndarray):
+def quantize_lhs(x: np.ndarray, fmt: str = "e4m3"):
     """1x128 block quantisation of ``x [M, K]``.
 
     Returns ``(codes [M, K] uint8, scales [M, K/128] fp32)`` (row-major scales;
@@ -74,12 +78,12 @@ def quantize_lhs(x: np.ndarray):
     assert K % BLOCK == 0
     t = torch.from_numpy(np.ascontiguousarray(x)).view(M, K // BLOCK, BLOCK)
     amax = t.abs().amax(dim=2)
-    s = _block_scale(amax)
-    codes = _encode(t / s.unsqueeze(2)).reshape(M, K)
+    s = _block_scale(amax, fmt)
+    codes = _encode(t / s.unsqueeze(2), fmt).reshape(M, K)
     return codes.numpy(), s.numpy()
 
 
-def quantize_rhs(x: np.ndarray):
+def quantize_rhs(x: np.ndarray, fmt: str = "e4m3"):
     """128x128 block quantisation of ``x [N, K]``.
 
     Returns ``(codes [N, K] uint8, scales [N/128, K/128] fp32)``.
@@ -88,8 +92,8 @@ def quantize_rhs(x: np.ndarray):
     assert N % BLOCK == 0 and K % BLOCK == 0
     t = torch.from_numpy(np.ascontiguousarray(x)).view(N // BLOCK, BLOCK, K // BLOCK, BLOCK)
     amax = t.abs().amax(dim=(1, 3))
-    s = _block_scale(amax)
-    codes = _encode(t / s[:, None, :, None]).reshape(N, K)
+    s = _block_scale(amax, fmt)
+    codes = _encode(t / s[:, None, :, None], fmt).reshape(N, K)
     return codes.numpy(), s.numpy()
 
 
@@ -135,20 +139,23 @@ class Masked:
     masked_m: np.ndarray  # int32 [G]
 
 
-def make_lhs(M: int, K: int, seed: int):
+def make_lhs(M: int, K: int, seed: int, fmt: str = "e4m3"):
     x = normal_with_outliers(np.random.Generator(np.random.PCG64(seed)), (M, K))
-    codes, s = quantize_lhs(x)
+    codes, s = quantize_lhs(x, fmt)
     return codes, np.ascontiguousarray(s.T)
 
 
-def make_rhs(N: int, K: int, seed):
+def make_rhs(N: int, K: int, seed, fmt: str = "e4m3"):
     x = normal_with_outliers(np.random.Generator(np.random.PCG64(seed)), (N, K))
-    return quantize_rhs(x)
+    return quantize_rhs(x, fmt)
 
 
-def make_dense(M: int, N: int, K: int, seed_a: int, seed_b: int) -> Dense:
-    a, sa_t = make_lhs(M, K, seed_a)
-    b, sb = make_rhs(N, K, seed_b)
+def make_dense(M: int, N: int, K: int, seed_a: int, seed_b: int, fmt_a: str = "e4m3",
+               fmt_b: str = "e4m3") -> Dense:
+    """Dense problem; the operand formats (e4m3 or e5m2, scale amax / format
+    maximum) only change the encoding, the recipe is the same."""
+    a, sa_t = make_lhs(M, K, seed_a, fmt_a)
+    b, sb = make_rhs(N, K, seed_b, fmt_b)
     return Dense(M, N, K, a, sa_t, b, sb)
 
 
