@@ -95,7 +95,11 @@ class Launcher:
             for i in range(n):
                 c = (a, sa, b, sb) if i == 0 else (a.clone(), sa.clone(), b.clone(), sb.clone())
                 self.copies.append(c)
-            self.fn = lambda c: ops.dg_fp8_gemm_nt(c[0], c[1].t(), c[2], c[3], d=d)
+            fa, fb = gen.CONFIGS[name].get("fmt", ("e4m3", "e4m3"))
+            if (fa, fb) == ("e4m3", "e4m3"):
+                self.fn = lambda c: ops.dg_fp8_gemm_nt(c[0], c[1].t(), c[2], c[3], d=d)
+            else:
+                self.fn = lambda c: ops.dg_fp8_gemm_nt_fmt(c[0], c[1].t(), c[2], c[3], fa, fb, d=d)
         elif self.kind == "contiguous":
             one = p.a.nbytes + p.b.nbytes
             n = max(1, min(8, -(-ROTATE_BYTES // one))) if rotate else 1

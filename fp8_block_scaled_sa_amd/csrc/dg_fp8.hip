@@ -166,7 +166,7 @@ int tile_override()
     return v;
 }
 
-template <int L, class C>
+template <int L, class C, int F = 0>
 int launch_tiles(dgk::Params &p, int groups, int cus, hipStream_t stream)
 {
     if (p.N % C::kBN != 0)
@@ -180,7 +180,7 @@ int launch_tiles(dgk::Params &p, int groups, int cus, hipStream_t stream)
     if (p.num_tiles == 0)
         return DG_OK;
     const int grid = p.num_tiles < cus ? p.num_tiles : cus;  // persistent: one workgroup per CU
-    hipLaunchKernelGGL((dgk::tile_kernel<L, C>), dim3(grid), dim3(C::kThreads), 0, stream, p);
+    hipLaunchKernelGGL((dgk::tile_kernel<L, C, F>), dim3(grid), dim3(C::kThreads), 0, stream, p);
     hipError_t e = hipGetLastError();
     return e == hipSuccess ? DG_OK : fail_hip(e);
 }
@@ -189,7 +189,7 @@ int launch_tiles(dgk::Params &p, int groups, int cus, hipStream_t stream)
 // (small M, or small M x N), each tile's K blocks are split over ks work items
 // (tiles * ks <= CUs, one round) that write fp32 partials; a second kernel
 // adds the slices in order and writes D.
-template <class C>
+template <class C, int F = 0>
 int launch_dense(dgk::Params &p, int cus, hipStream_t stream)
 {
     if (p.N % C::kBN != 0)
@@ -205,7 +205,7 @@ int launch_dense(dgk::Params &p, int cus, hipStream_t stream)
             ks = 1;
     }
     p.ksplit = ks;
-    int st = launch_tiles<dgk::kDense, C>(p, ks, cus, stream);
+    int st = launch_tiles<dgk::kDense, C, F>(p, ks, cus, stream);
     if (st != DG_OK || ks == 1)
         return st;
     const int64_t quads = (int64_t)p.M * (p.N / 4);
@@ -248,6 +248,7 @@ TileCut round_cut(int64_t tiles_m, int64_t tiles_n, int cus)
 // Dense GEMM, configuration chosen from the shape: 256x256 tiles while they
 // fill the CUs (a last round at most half full is cut off and run with
 // smaller tiles); below that, smaller tiles split over K.
+template <int F = 0>
 int launch_dense_auto(dgk::Params &p, int cus, hipStream_t s)
 {
     const bool wide_n = p.N % 256 == 0;
@@ -255,7 +256,7 @@ int launch_dense_auto(dgk::Params &p, int cus, hipStream_t s)
     if (wide_n && tiles_m * tiles_n * 2 > cus) {
         const TileCut c = round_cut(tiles_m, tiles_n, cus);
         if (c.cut_n == 0 && c.cut_m == 0)
-            return launch_dense<CfgBig>(p, cus, s);
+            return launch_dense<CfgBig, F>(p, cus, s);
         dgk::Params main = p, rest = p;
         if (c.cut_n) {  // columns [0, N1) whole rounds; the rest on 256x128 tiles
             const int64_t N1 = 256 * c.cut_n;
@@ -272,14 +273,14 @@ int launch_dense_auto(dgk::Params &p, int cus, hipStream_t s)
             rest.D += M1 * p.ldd;
             rest.M = p.M - (int)M1;
         }
-        const int st = launch_dense<CfgBig>(main, cus, s);
+        const int st = launch_dense<CfgBig, F>(main, cus, s);
         if (st != DG_OK)
             return st;
-        return c.cut_n ? launch_dense<CfgDense>(rest, cus, s) : launch_dense_auto(rest, cus, s);
+        return c.cut_n ? launch_dense<CfgDense, F>(rest, cus, s) : launch_dense_auto<F>(rest, cus, s);
     }
     if (p.M <= 128)
-        return launch_dense<CfgNarrow>(p, cus, s);
-    return launch_dense<CfgDense>(p, cus, s);
+        return launch_dense<CfgNarrow, F>(p, cus, s);
+    return launch_dense<CfgDense, F>(p, cus, s);
 }
 
 // Per-lane DMA offsets are 32-bit: a tile's rows of A, B and sA must span < 2^32 bytes.
@@ -455,6 +456,46 @@ int quantize_impl(const void *X, int x_dtype, int64_t ldx, int64_t x_rows, const
     return e == hipSuccess ? DG_OK : fail_hip(e);
 }
 
+// Validation and kernel arguments of a dense call. Returns DG_OK with `p`
+// and `dev` filled, kEmptyProblem for an empty problem, or an error.
+constexpr int kEmptyProblem = -2;
+
+int dense_setup(const void *A, int64_t lda, const float *sA, int64_t sa_stride_m, int64_t sa_stride_kb,
+                const void *B, int64_t ldb, const float *sB, int64_t sb_stride_nb, int64_t sb_stride_kb,
+                void *D, int64_t ldd, int64_t M, int64_t N, int64_t K, dgk::Params &p, DeviceInfo &dev)
+{
+    int st = check_common_shape(M, N, K);
+    if (st != DG_OK)
+        return st;
+    if (M == 0 || N == 0)
+        return kEmptyProblem;
+    if (!A || !sA || !B || !sB || !D)
+        return DG_ERR_NULL_POINTER;
+    if (lda < K || ldb < K || ldd < N || sa_stride_m < 0 || sa_stride_kb < 0 || sb_stride_nb < 0 ||
+        sb_stride_kb < 0)
+        return DG_ERR_BAD_STRIDE;
+    if (!aligned(A, 16) || !aligned(B, 16) || !aligned(D, 16) || lda % 16 || ldb % 16 || ldd % 8 ||
+        !aligned(sA, 4) || !aligned(sB, 4))
+        return DG_ERR_MISALIGNED;
+    const int64_t nkb = K / 128;
+    const Extent ed = extent(D, 2, (M - 1) * ldd + N - 1);
+    if (overlaps(ed, extent(A, 1, (M - 1) * lda + K - 1)) || overlaps(ed, extent(B, 1, (N - 1) * ldb + K - 1)) ||
+        overlaps(ed, extent(sA, 4, last_scale_index(M, nkb, sa_stride_m, sa_stride_kb))) ||
+        overlaps(ed, extent(sB, 4, last_scale_index(N / 128, nkb, sb_stride_nb, sb_stride_kb))))
+        return DG_ERR_ALIASING;
+    if ((st = current_device(dev)) != DG_OK)
+        return st;
+
+    p = dgk::Params{};
+    p.A = (const uint8_t *)A; p.lda = lda;
+    p.sA = sA; p.sa_m = sa_stride_m; p.sa_kb = sa_stride_kb;
+    p.B = (const uint8_t *)B; p.ldb = ldb;
+    p.sB = sB; p.sb_nb = sb_stride_nb; p.sb_kb = sb_stride_kb;
+    p.D = (uint16_t *)D; p.ldd = ldd;
+    p.M = (int)M; p.N = (int)N; p.K = (int)K; p.G = 1;
+    return DG_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -482,36 +523,13 @@ int dg_fp8_gemm_nt(const void *A, int64_t lda, const float *sA, int64_t sa_strid
                    const void *B, int64_t ldb, const float *sB, int64_t sb_stride_nb, int64_t sb_stride_kb,
                    void *D, int64_t ldd, int64_t M, int64_t N, int64_t K, void *stream)
 {
-    int st = check_common_shape(M, N, K);
-    if (st != DG_OK)
-        return st;
-    if (M == 0 || N == 0)
-        return DG_OK;
-    if (!A || !sA || !B || !sB || !D)
-        return DG_ERR_NULL_POINTER;
-    if (lda < K || ldb < K || ldd < N || sa_stride_m < 0 || sa_stride_kb < 0 || sb_stride_nb < 0 ||
-        sb_stride_kb < 0)
-        return DG_ERR_BAD_STRIDE;
-    if (!aligned(A, 16) || !aligned(B, 16) || !aligned(D, 16) || lda % 16 || ldb % 16 || ldd % 8 ||
-        !aligned(sA, 4) || !aligned(sB, 4))
-        return DG_ERR_MISALIGNED;
-    const int64_t nkb = K / 128;
-    const Extent ed = extent(D, 2, (M - 1) * ldd + N - 1);
-    if (overlaps(ed, extent(A, 1, (M - 1) * lda + K - 1)) || overlaps(ed, extent(B, 1, (N - 1) * ldb + K - 1)) ||
-        overlaps(ed, extent(sA, 4, last_scale_index(M, nkb, sa_stride_m, sa_stride_kb))) ||
-        overlaps(ed, extent(sB, 4, last_scale_index(N / 128, nkb, sb_stride_nb, sb_stride_kb))))
-        return DG_ERR_ALIASING;
+    dgk::Params p;
     DeviceInfo dev;
-    if ((st = current_device(dev)) != DG_OK)
-        return st;
-
-    dgk::Params p = {};
-    p.A = (const uint8_t *)A; p.lda = lda;
-    p.sA = sA; p.sa_m = sa_stride_m; p.sa_kb = sa_stride_kb;
-    p.B = (const uint8_t *)B; p.ldb = ldb;
-    p.sB = sB; p.sb_nb = sb_stride_nb; p.sb_kb = sb_stride_kb;
-    p.D = (uint16_t *)D; p.ldd = ldd;
-    p.M = (int)M; p.N = (int)N; p.K = (int)K; p.G = 1;
+    int st = dense_setup(A, lda, sA, sa_stride_m, sa_stride_kb, B, ldb, sB, sb_stride_nb, sb_stride_kb, D, ldd,
+                         M, N, K, p, dev);
+    if (st != DG_OK)
+        return st == kEmptyProblem ? DG_OK : st;
+    const int64_t nkb = K / 128;
     hipStream_t s = (hipStream_t)stream;
     // M <= 64: the decode kernels (B streamed once per launch, the LHS staged
     // per wave 16 rows at a time). Where their LDS staging does not fit the
@@ -652,6 +670,33 @@ int dg_fp8_grouped_gemm_masked(const void *A, int64_t lda, int64_t a_stride_g, c
         if (N % 256 == 0)
             return launch_tiles<dgk::kMasked, CfgBigStreamB>(p, (int)G, dev.cus, (hipStream_t)stream);
         return launch_tiles<dgk::kMasked, CfgDense>(p, (int)G, dev.cus, (hipStream_t)stream);
+    }
+}
+
+int dg_fp8_gemm_nt_fmt(const void *A, int a_fmt, int64_t lda, const float *sA, int64_t sa_stride_m,
+                       int64_t sa_stride_kb, const void *B, int b_fmt, int64_t ldb, const float *sB,
+                       int64_t sb_stride_nb, int64_t sb_stride_kb, void *D, int64_t ldd, int64_t M, int64_t N,
+                       int64_t K, void *stream)
+{
+    if ((a_fmt != DG_FP8_E4M3 && a_fmt != DG_FP8_E5M2) || (b_fmt != DG_FP8_E4M3 && b_fmt != DG_FP8_E5M2))
+        return DG_ERR_UNSUPPORTED;
+    if (a_fmt == DG_FP8_E4M3 && b_fmt == DG_FP8_E4M3)
+        return dg_fp8_gemm_nt(A, lda, sA, sa_stride_m, sa_stride_kb, B, ldb, sB, sb_stride_nb, sb_stride_kb, D,
+                              ldd, M, N, K, stream);
+    dgk::Params p;
+    DeviceInfo dev;
+    int st = dense_setup(A, lda, sA, sa_stride_m, sa_stride_kb, B, ldb, sB, sb_stride_nb, sb_stride_kb, D, ldd,
+                         M, N, K, p, dev);
+    if (st != DG_OK)
+        return st == kEmptyProblem ? DG_OK : st;
+    if (!offsets_fit(lda, ldb, sa_stride_m))
+        return DG_ERR_UNSUPPORTED;
+    hipStream_t s = (hipStream_t)stream;
+    // Formats other than e4m3 x e4m3 run on the tile kernel at every M.
+    switch ((a_fmt == DG_FP8_E5M2 ? 1 : 0) | (b_fmt == DG_FP8_E5M2 ? 2 : 0)) {
+    case 1: return launch_dense_auto<1>(p, dev.cus, s);
+    case 2: return launch_dense_auto<2>(p, dev.cus, s);
+    default: return launch_dense_auto<3>(p, dev.cus, s);
     }
 }
 

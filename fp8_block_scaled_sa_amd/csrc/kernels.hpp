@@ -69,6 +69,17 @@ __device__ __forceinline__ v4f mfma_e4m3_16x16x128(const v8i &a, const v8i &b)
     return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, zero, 0, 0, 0, 0, 0, 0);
 }
 
+// Operand formats of the tile kernel: bit 0 set = the GEMM's A holds e5m2,
+// bit 1 set = B holds e5m2 (else e4m3). The MFMA takes them as its format
+// selectors (0 = e4m3, 1 = e5m2): the first MFMA operand is fed from B, the
+// second from A (see the orientation above).
+template <int F>
+__device__ __forceinline__ v4f mfma_fmt_16x16x128(const v8i &b_rows, const v8i &a_rows)
+{
+    const v4f zero = {0.f, 0.f, 0.f, 0.f};
+    return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(b_rows, a_rows, zero, (F >> 1) & 1, F & 1, 0, 0, 0, 0);
+}
+
 // fp32 -> bf16 bits, round to nearest even (NaN stays NaN).
 __device__ __forceinline__ uint32_t bf16_rne(float f)
 {
@@ -285,7 +296,7 @@ __device__ __forceinline__ void wait_stage(int per_stage)
         wait_vmcnt<(SEGW + 2) * LATER>();
 }
 
-template <int L, class C>
+template <int L, class C, int F = 0>
 __global__ void __launch_bounds__(C::kThreads, 1) tile_kernel(Params p)
 {
     constexpr int BM = C::kBM, BN = C::kBN, S = C::kStages;
@@ -500,7 +511,7 @@ __global__ void __launch_bounds__(C::kThreads, 1) tile_kernel(Params p)
                 const float sc = part_sc;
 #pragma unroll
                 for (int j = 0; j < NJ; ++j) {
-                    const v4f nx = mfma_e4m3_16x16x128(bf[j], af[i & 1]);
+                    const v4f nx = mfma_fmt_16x16x128<F>(bf[j], af[i & 1]);
                     if (i == 0)
                         acc[MI - 1][j] += part[j] * sc;
                     else

@@ -79,6 +79,34 @@ def dg_fp8_gemm_nt(a, sa, b, sb, d=None, stream=None):
     return d
 
 
+FORMATS = {"e4m3": 0, "e5m2": 1}   # DG_FP8_E4M3, DG_FP8_E5M2
+
+
+def dg_fp8_gemm_nt_fmt(a, sa, b, sb, a_fmt="e4m3", b_fmt="e4m3", d=None, stream=None):
+    """dg_fp8_gemm_nt with a per-operand fp8 format ("e4m3" or "e5m2"). Codes
+    are uint8 (or the matching torch float8 dtype)."""
+    for t, name in ((a, "a"), (b, "b")):
+        if t.dtype not in (torch.uint8, torch.float8_e4m3fn, torch.float8_e5m2) or t.dim() != 2 or t.stride(-1) != 1:
+            raise TypeError("%s must be a 2-D fp8 code tensor with a contiguous last (K) dimension" % name)
+    _scales(sa, "sa", 2), _scales(sb, "sb", 2)
+    M, K = a.shape
+    N = b.shape[0]
+    if d is None:
+        d = torch.empty((M, N), dtype=torch.bfloat16, device=a.device)
+    if d.dtype != torch.bfloat16 or d.dim() != 2 or d.stride(-1) != 1:
+        raise TypeError("d must be a 2-D bfloat16 tensor with contiguous rows")
+    if b.shape[1] != K or tuple(d.shape) != (M, N):
+        raise ValueError("shape mismatch")
+    if tuple(sa.shape) != (M, K // BLOCK) or tuple(sb.shape) != (N // BLOCK, K // BLOCK):
+        raise ValueError("scale shape mismatch")
+    lib = _lib.load()
+    st = lib.dg_fp8_gemm_nt_fmt(_dev(a, "a"), FORMATS[a_fmt], a.stride(0), _dev(sa, "sa"), sa.stride(0), sa.stride(1),
+                                _dev(b, "b"), FORMATS[b_fmt], b.stride(0), _dev(sb, "sb"), sb.stride(0), sb.stride(1),
+                                _dev(d, "d"), d.stride(0), M, N, K, _stream(stream))
+    _check(st, "dg_fp8_gemm_nt_fmt")
+    return d
+
+
 def dg_fp8_grouped_gemm_contiguous(a, sa, b, sb, expert_ids, d=None, stream=None):
     """Contiguous MoE layout: A[M_total,K], sA[M_total,K/128], B[G,N,K],
     sB[G,N/128,K/128], expert_ids[M_total] int32 -> D[M_total,N]; rows whose

@@ -119,6 +119,29 @@ int dg_fp8_gemm_nt(const void *A, int64_t lda,
                    void *D, int64_t ldd,
                    int64_t M, int64_t N, int64_t K, void *stream);
 
+/* Operand formats of dg_fp8_gemm_nt_fmt. */
+#define DG_FP8_E4M3 0
+#define DG_FP8_E5M2 1
+
+/*
+ * Dense NT GEMM with a choice of fp8 format per operand: OCP e4m3 (largest
+ * finite 448) or e5m2 (1 sign, 5 exponent bits with bias 15, 2 mantissa
+ * bits, largest finite 57344): rkmt.cn walkthrough §2.1; mixing an e4m3 A
+ * with an e5m2 B trades precision for range: lpnh.cn article §2.1. The
+ * operation, the scale granularity, the arguments and the errors are those
+ * of dg_fp8_gemm_nt; a_fmt / b_fmt are DG_FP8_E4M3 or DG_FP8_E5M2 (else
+ * DG_ERR_UNSUPPORTED). Infinity and NaN codes in an operand give unspecified
+ * results. With both operands e4m3 this is dg_fp8_gemm_nt; every other
+ * combination runs on the tile kernel at every M (split over K, with the
+ * same workspace rules, when its tiles are few).
+ */
+int dg_fp8_gemm_nt_fmt(const void *A, int a_fmt, int64_t lda,
+                       const float *sA, int64_t sa_stride_m, int64_t sa_stride_kb,
+                       const void *B, int b_fmt, int64_t ldb,
+                       const float *sB, int64_t sb_stride_nb, int64_t sb_stride_kb,
+                       void *D, int64_t ldd,
+                       int64_t M, int64_t N, int64_t K, void *stream);
+
 /*
  * Grouped GEMM, contiguous layout (MoE): the rows of all experts are stacked
  * in one LHS, each expert's rows contiguous and padded to a multiple of 128,

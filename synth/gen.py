@@ -231,6 +231,7 @@ CONFIGS = {
     "dense_64x256x512": dict(kind="dense", M=64, N=256, K=512, seeds=(101, 102)),
     "decode_8x4096x7168": dict(kind="dense", M=8, N=4096, K=7168, seeds=(201, 202)),
     "square_4096": dict(kind="dense", M=4096, N=4096, K=4096, seeds=(301, 302)),
+    "square_4096_e4m3xe5m2": dict(kind="dense", M=4096, N=4096, K=4096, seeds=(301, 302), fmt=("e4m3", "e5m2")),
     "prefill_8192x7168x2048": dict(kind="dense", M=8192, N=7168, K=2048, seeds=(311, 312)),
     "moe_contiguous_g8_t8192": dict(kind="contiguous", G=8, tokens=8192, N=4096, K=7168,
                                     seeds=(401, 402, 403)),
@@ -256,7 +257,7 @@ def make_activations(name: str) -> np.ndarray:
 def make_config(name: str):
     c = CONFIGS[name]
     if c["kind"] == "dense":
-        return make_dense(c["M"], c["N"], c["K"], *c["seeds"])
+        return make_dense(c["M"], c["N"], c["K"], *c["seeds"], *c.get("fmt", ("e4m3", "e4m3")))
     if c["kind"] == "contiguous":
         return make_contiguous(c["G"], c["tokens"], c["N"], c["K"], *c["seeds"])
     return make_masked(c["G"], c["M_max"], c["N"], c["K"], *c["seeds"])

@@ -266,3 +266,28 @@ def test_unpermute_validation(kw, status):
 
 def test_unpermute_empty():
     assert unperm(T=0) == DG_OK
+
+
+def nt_fmt(a_fmt=1, b_fmt=0, **kw):
+    args = dict(A=A, a_fmt=a_fmt, lda=512, sA=SA, sa_m=1, sa_kb=64, B=B, b_fmt=b_fmt, ldb=512, sB=SB, sb_nb=4,
+                sb_kb=1, D=D, ldd=256, M=64, N=256, K=512, stream=None)
+    args.update(kw)
+    return _lib.load().dg_fp8_gemm_nt_fmt(*args.values())
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(a_fmt=2), DG_ERR_UNSUPPORTED),
+    (dict(b_fmt=-1), DG_ERR_UNSUPPORTED),
+    (dict(K=500, lda=512, ldb=512), DG_ERR_BAD_SHAPE),
+    (dict(A=None), DG_ERR_NULL_POINTER),
+    (dict(lda=256), DG_ERR_BAD_STRIDE),
+    (dict(D=D + 2), DG_ERR_MISALIGNED),
+    (dict(D=SB), DG_ERR_ALIASING),
+    (dict(a_fmt=0, b_fmt=0, D=SB), DG_ERR_ALIASING),     # e4m3 x e4m3 goes through dg_fp8_gemm_nt
+])
+def test_fmt_validation(kw, status):
+    assert nt_fmt(**kw) == status
+
+
+def test_fmt_empty():
+    assert nt_fmt(M=0) == DG_OK and nt_fmt(a_fmt=1, b_fmt=1, N=0) == DG_OK
