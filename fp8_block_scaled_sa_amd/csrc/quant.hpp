@@ -117,8 +117,10 @@ __global__ __launch_bounds__(64 * kWavesPerGroup) void quantize_1x128_kernel(Qua
     const int64_t unit = (int64_t)wg * kWavesPerGroup + (threadIdx.x >> 6);
     if (unit >= p.units)
         return;
-    const int row = (int)(unit / p.spans);
-    const int span = (int)(unit - (int64_t)row * p.spans);
+    // row and span are the same for every lane of the wave: keep them (and the
+    // source-row lookup) in scalar registers
+    const int row = __builtin_amdgcn_readfirstlane((int)(unit / p.spans));
+    const int span = __builtin_amdgcn_readfirstlane((int)(unit - (int64_t)row * p.spans));
     const int64_t src = p.src_rows ? (int64_t)p.src_rows[row] : (int64_t)row;
     const bool present = src >= 0 && src < p.x_rows;
     const int nkb = p.K >> 7;
