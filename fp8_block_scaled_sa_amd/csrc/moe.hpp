@@ -17,7 +17,8 @@
 // remaining lane's id, so a chunk costs one round per distinct expert in it.
 // Pass 1 counts per (wave, expert); an exclusive prefix over the waves and a
 // scan over the padded segment sizes give every token's row in pass 2. No
-// atomics: the result is the same on every run.
+// atomics: the result is the same on every run. With at most 64 experts the
+// per-wave counts stay in registers (lane j: expert j) during both passes.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -54,6 +55,10 @@ __device__ __forceinline__ void load_experts(const RouteParams &p, int base, int
     }
 }
 
+// SMALL (G <= 64): lane j of each wave keeps expert j's count in a register,
+// read and updated with v_readlane / a lane-predicated add, so a ballot round
+// does no LDS traffic. Otherwise the counts live in LDS.
+template <bool SMALL>
 __global__ __launch_bounds__(kRouteThreads) void route_contiguous_kernel(RouteParams p)
 {
     __shared__ int cnt[kRouteWaves][kMaxExperts];  // per-wave counts, then per-wave running offsets
@@ -67,6 +72,7 @@ __global__ __launch_bounds__(kRouteThreads) void route_contiguous_kernel(RoutePa
 
     const int chunk = (p.T + kRouteWaves - 1) / kRouteWaves;
     const int t0 = min(p.T, w * chunk), t1 = min(p.T, t0 + chunk);
+    int mine = 0;  // SMALL: this wave's count of expert `lane`
     for (int sc = t0; sc < t1; sc += 64 * kChunks) {
         int ex[kChunks];
         load_experts(p, sc, t1, lane, ex);
@@ -78,14 +84,20 @@ __global__ __launch_bounds__(kRouteThreads) void route_contiguous_kernel(RoutePa
             uint64_t todo = __ballot(e >= 0);
             while (todo) {
                 const int leader = __ffsll((unsigned long long)todo) - 1;
-                const int el = __shfl(e, leader);
+                const int el = __builtin_amdgcn_readlane(e, leader);
                 const uint64_t same = __ballot(e == el);
-                if (lane == leader)
+                if (SMALL) {
+                    if (lane == el)
+                        mine += __popcll(same);
+                } else if (lane == leader) {
                     cnt[w][el] += __popcll(same);
+                }
                 todo &= ~same;
             }
         }
     }
+    if (SMALL && lane < p.G)
+        cnt[w][lane] = mine;
     __syncthreads();
 
     const int e = threadIdx.x;  // G <= kMaxExperts == kRouteThreads: one expert per thread
@@ -127,6 +139,8 @@ __global__ __launch_bounds__(kRouteThreads) void route_contiguous_kernel(RoutePa
         p.token_of_row[r] = -1;
     }
 
+    // SMALL: lane j holds the next row of expert j for this wave
+    int next = (SMALL && lane < p.G) ? seg[lane] + cnt[w][lane] : 0;
     for (int sc = t0; sc < t1; sc += 64 * kChunks) {
         int ex[kChunks];
         load_experts(p, sc, t1, lane, ex);
@@ -140,12 +154,21 @@ __global__ __launch_bounds__(kRouteThreads) void route_contiguous_kernel(RoutePa
             int row = -1;
             while (todo) {
                 const int leader = __ffsll((unsigned long long)todo) - 1;
-                const int el = __shfl(e, leader);
+                const int el = __builtin_amdgcn_readlane(e, leader);
                 const uint64_t same = __ballot(e == el);
-                if (e == el)
-                    row = seg[el] + cnt[w][el] + __popcll(same & ((1ull << lane) - 1));
-                if (lane == leader)
-                    cnt[w][el] += __popcll(same);
+                const int rank = __popcll(same & ((1ull << lane) - 1));
+                if (SMALL) {
+                    const int base = __builtin_amdgcn_readlane(next, el);
+                    if (e == el)
+                        row = base + rank;
+                    if (lane == el)
+                        next += __popcll(same);
+                } else {
+                    if (e == el)
+                        row = seg[el] + cnt[w][el] + rank;
+                    if (lane == leader)
+                        cnt[w][el] += __popcll(same);
+                }
                 todo &= ~same;
             }
             if (t < t1) {
