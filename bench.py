@@ -226,8 +226,9 @@ def time_moe_layer(steps, warmup):
     """The contiguous MoE step end to end on the contiguous workload's shape
     (8 experts, 8192 tokens, K 7168, N 4096, top-1 routing seed): routing ->
     bf16 activations quantised into the padded layout -> grouped GEMM over
-    the layout's capacity -> rows back in token order. Whole step timed as one
-    graph of `steps` repetitions; each stage also timed on its own."""
+    the layout's capacity, written straight to token order. Whole step timed
+    as one graph of `steps` repetitions; also the step with a separate
+    un-permute, and each stage on its own."""
     import torch
     from fp8_block_scaled_sa_amd import ops
     from synth import gen
@@ -267,7 +268,13 @@ def time_moe_layer(steps, warmup):
     def unperm(i):
         ops.dg_moe_unpermute(d, row, out=out)
 
-    def step(i):
+    def gemm_to_tokens(i):
+        ops.dg_fp8_grouped_gemm_contiguous_to_tokens(q, s, bs[i % n], sbd, ids, tok, T, out=out)
+
+    def step(i):  # the un-permute folded into the GEMM's epilogue
+        route(i), quant(i), gemm_to_tokens(i)
+
+    def step_unfused(i):
         route(i), quant(i), gemm(i), unperm(i)
 
     def graph_us(fn):
@@ -292,10 +299,13 @@ def time_moe_layer(steps, warmup):
         return a.elapsed_time(z) * 1e3 / steps
 
     total = graph_us(step)
+    unfused = graph_us(step_unfused)
     stages = {k: round(graph_us(f), 2) for k, f in (("route", route), ("quantize_gather", quant),
+                                                    ("grouped_gemm_to_tokens", gemm_to_tokens),
                                                     ("grouped_gemm", gemm), ("unpermute", unperm))}
     flops = 2 * T * N * K
-    return {"us_per_step": round(total, 2), "tflops": round(flops / total / 1e6, 1),
+    return {"us_per_step": round(total, 2), "us_per_step_unfused": round(unfused, 2),
+            "tflops": round(flops / total / 1e6, 1),
             "frac_fp8_peak": round(flops / total / 1e6 / FP8_PEAK_TFLOPS, 4), "stages_us": stages,
             "rows_used": int(layout[G].item()), "rows_capacity": M_cap, "operand_copies": n}
 

@@ -21,6 +21,9 @@ SIGNATURES = {
     "dg_fp8_grouped_gemm_contiguous": (ctypes.c_int, [_p, _i64, _p, _i64, _i64, _p, _i64, _i64,
                                                       _p, _i64, _i64, _i64, _p, _p, _i64,
                                                       _i64, _i64, _i64, _i64, _p]),
+    "dg_fp8_grouped_gemm_contiguous_to_tokens": (ctypes.c_int, [_p, _i64, _p, _i64, _i64, _p, _i64, _i64,
+                                                                _p, _i64, _i64, _i64, _p, _p, _p, _i64, _i64,
+                                                                _i64, _i64, _i64, _i64, _p]),
     "dg_fp8_grouped_gemm_masked": (ctypes.c_int, [_p, _i64, _i64, _p, _i64, _i64, _i64,
                                                   _p, _i64, _i64, _p, _i64, _i64, _i64, _p,
                                                   _p, _i64, _i64, _i64, _i64, _i64, _i64, _p]),

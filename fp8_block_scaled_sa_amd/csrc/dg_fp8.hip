@@ -166,7 +166,7 @@ int tile_override()
     return v;
 }
 
-template <int L, class C, int F = 0>
+template <int L, class C, int F = 0, bool SCATTER = false>
 int launch_tiles(dgk::Params &p, int groups, int cus, hipStream_t stream)
 {
     if (p.N % C::kBN != 0)
@@ -180,7 +180,7 @@ int launch_tiles(dgk::Params &p, int groups, int cus, hipStream_t stream)
     if (p.num_tiles == 0)
         return DG_OK;
     const int grid = p.num_tiles < cus ? p.num_tiles : cus;  // persistent: one workgroup per CU
-    hipLaunchKernelGGL((dgk::tile_kernel<L, C, F>), dim3(grid), dim3(C::kThreads), 0, stream, p);
+    hipLaunchKernelGGL((dgk::tile_kernel<L, C, F, SCATTER>), dim3(grid), dim3(C::kThreads), 0, stream, p);
     hipError_t e = hipGetLastError();
     return e == hipSuccess ? DG_OK : fail_hip(e);
 }
@@ -496,6 +496,79 @@ int dense_setup(const void *A, int64_t lda, const float *sA, int64_t sa_stride_m
     return DG_OK;
 }
 
+// The contiguous grouped GEMM. With token_of_row, row r of the result is
+// written to row token_of_row[r] of D (D has d_rows rows); without it, to row r
+// (d_rows = M_total).
+int contiguous_impl(const void *A, int64_t lda, const float *sA, int64_t sa_stride_m, int64_t sa_stride_kb,
+                    const void *B, int64_t ldb, int64_t b_stride_g, const float *sB, int64_t sb_stride_g,
+                    int64_t sb_stride_nb, int64_t sb_stride_kb, const int32_t *expert_ids,
+                    const int32_t *token_of_row, void *D, int64_t ldd, int64_t d_rows, int64_t M_total, int64_t N,
+                    int64_t K, int64_t G, void *stream)
+{
+    int st = check_common_shape(M_total, N, K);
+    if (st != DG_OK)
+        return st;
+    if (G < 0 || M_total % 128 != 0)
+        return DG_ERR_BAD_SHAPE;
+    if (G > kInt32Max)
+        return DG_ERR_UNSUPPORTED;
+    if (d_rows < 0)
+        return DG_ERR_BAD_SHAPE;
+    if (d_rows > kInt32Max)
+        return DG_ERR_UNSUPPORTED;
+    if (M_total == 0 || N == 0 || G == 0 || d_rows == 0)
+        return DG_OK;
+    if (!A || !sA || !B || !sB || !expert_ids || !D)
+        return DG_ERR_NULL_POINTER;
+    if (token_of_row && !aligned(token_of_row, 4))
+        return DG_ERR_MISALIGNED;
+    if (lda < K || ldb < K || ldd < N || sa_stride_m < 0 || sa_stride_kb < 0 || sb_stride_nb < 0 ||
+        sb_stride_kb < 0 || sb_stride_g < 0 || (G > 1 && b_stride_g < (N - 1) * ldb + K))
+        return DG_ERR_BAD_STRIDE;
+    if (!aligned(A, 16) || !aligned(B, 16) || !aligned(D, 16) || lda % 16 || ldb % 16 || b_stride_g % 16 ||
+        ldd % 8 || !aligned(sA, 4) || !aligned(sB, 4) || !aligned(expert_ids, 4))
+        return DG_ERR_MISALIGNED;
+    const int64_t nkb = K / 128;
+    const Extent ed = extent(D, 2, (d_rows - 1) * ldd + N - 1);
+    if (token_of_row && overlaps(ed, extent(token_of_row, 4, M_total - 1)))
+        return DG_ERR_ALIASING;
+    if (overlaps(ed, extent(A, 1, (M_total - 1) * lda + K - 1)) ||
+        overlaps(ed, extent(B, 1, (G - 1) * b_stride_g + (N - 1) * ldb + K - 1)) ||
+        overlaps(ed, extent(sA, 4, last_scale_index(M_total, nkb, sa_stride_m, sa_stride_kb))) ||
+        overlaps(ed, extent(sB, 4, (G - 1) * sb_stride_g + last_scale_index(N / 128, nkb, sb_stride_nb, sb_stride_kb))) ||
+        overlaps(ed, extent(expert_ids, 4, M_total - 1)))
+        return DG_ERR_ALIASING;
+    DeviceInfo dev;
+    if ((st = current_device(dev)) != DG_OK)
+        return st;
+
+    dgk::Params p = {};
+    p.A = (const uint8_t *)A; p.lda = lda;
+    p.sA = sA; p.sa_m = sa_stride_m; p.sa_kb = sa_stride_kb;
+    p.B = (const uint8_t *)B; p.ldb = ldb; p.b_stride_g = b_stride_g;
+    p.sB = sB; p.sb_nb = sb_stride_nb; p.sb_kb = sb_stride_kb; p.sb_g = sb_stride_g;
+    p.D = (uint16_t *)D; p.ldd = ldd;
+    p.ids = expert_ids;
+    p.row_dst = token_of_row; p.dst_rows = (int)d_rows;
+    p.M = (int)M_total; p.N = (int)N; p.K = (int)K; p.G = (int)G;
+    if (!offsets_fit(lda, ldb, sa_stride_m))
+        return DG_ERR_UNSUPPORTED;
+    if (token_of_row) {
+        if (N % 256 == 0)
+            return launch_tiles<dgk::kContiguous, CfgBig, 0, true>(p, 1, dev.cus, (hipStream_t)stream);
+        return launch_tiles<dgk::kContiguous, CfgDense, 0, true>(p, 1, dev.cus, (hipStream_t)stream);
+    }
+    switch (tile_override()) {
+    case 2: return launch_tiles<dgk::kContiguous, CfgNarrow>(p, 1, dev.cus, (hipStream_t)stream);
+    case 3: return launch_tiles<dgk::kContiguous, CfgWide>(p, 1, dev.cus, (hipStream_t)stream);
+    case 4: return launch_tiles<dgk::kContiguous, CfgDense>(p, 1, dev.cus, (hipStream_t)stream);
+    default:
+        if (N % 256 == 0)
+            return launch_tiles<dgk::kContiguous, CfgBig>(p, 1, dev.cus, (hipStream_t)stream);
+        return launch_tiles<dgk::kContiguous, CfgDense>(p, 1, dev.cus, (hipStream_t)stream);
+    }
+}
+
 }  // namespace
 
 extern "C" {
@@ -562,54 +635,23 @@ int dg_fp8_grouped_gemm_contiguous(const void *A, int64_t lda, const float *sA, 
                                    const int32_t *expert_ids, void *D, int64_t ldd, int64_t M_total, int64_t N,
                                    int64_t K, int64_t G, void *stream)
 {
-    int st = check_common_shape(M_total, N, K);
-    if (st != DG_OK)
-        return st;
-    if (G < 0 || M_total % 128 != 0)
-        return DG_ERR_BAD_SHAPE;
-    if (G > kInt32Max)
-        return DG_ERR_UNSUPPORTED;
-    if (M_total == 0 || N == 0 || G == 0)
-        return DG_OK;
-    if (!A || !sA || !B || !sB || !expert_ids || !D)
-        return DG_ERR_NULL_POINTER;
-    if (lda < K || ldb < K || ldd < N || sa_stride_m < 0 || sa_stride_kb < 0 || sb_stride_nb < 0 ||
-        sb_stride_kb < 0 || sb_stride_g < 0 || (G > 1 && b_stride_g < (N - 1) * ldb + K))
-        return DG_ERR_BAD_STRIDE;
-    if (!aligned(A, 16) || !aligned(B, 16) || !aligned(D, 16) || lda % 16 || ldb % 16 || b_stride_g % 16 ||
-        ldd % 8 || !aligned(sA, 4) || !aligned(sB, 4) || !aligned(expert_ids, 4))
-        return DG_ERR_MISALIGNED;
-    const int64_t nkb = K / 128;
-    const Extent ed = extent(D, 2, (M_total - 1) * ldd + N - 1);
-    if (overlaps(ed, extent(A, 1, (M_total - 1) * lda + K - 1)) ||
-        overlaps(ed, extent(B, 1, (G - 1) * b_stride_g + (N - 1) * ldb + K - 1)) ||
-        overlaps(ed, extent(sA, 4, last_scale_index(M_total, nkb, sa_stride_m, sa_stride_kb))) ||
-        overlaps(ed, extent(sB, 4, (G - 1) * sb_stride_g + last_scale_index(N / 128, nkb, sb_stride_nb, sb_stride_kb))) ||
-        overlaps(ed, extent(expert_ids, 4, M_total - 1)))
-        return DG_ERR_ALIASING;
-    DeviceInfo dev;
-    if ((st = current_device(dev)) != DG_OK)
-        return st;
+    return contiguous_impl(A, lda, sA, sa_stride_m, sa_stride_kb, B, ldb, b_stride_g, sB, sb_stride_g,
+                           sb_stride_nb, sb_stride_kb, expert_ids, nullptr, D, ldd, M_total, M_total, N, K, G,
+                           stream);
+}
 
-    dgk::Params p = {};
-    p.A = (const uint8_t *)A; p.lda = lda;
-    p.sA = sA; p.sa_m = sa_stride_m; p.sa_kb = sa_stride_kb;
-    p.B = (const uint8_t *)B; p.ldb = ldb; p.b_stride_g = b_stride_g;
-    p.sB = sB; p.sb_nb = sb_stride_nb; p.sb_kb = sb_stride_kb; p.sb_g = sb_stride_g;
-    p.D = (uint16_t *)D; p.ldd = ldd;
-    p.ids = expert_ids;
-    p.M = (int)M_total; p.N = (int)N; p.K = (int)K; p.G = (int)G;
-    if (!offsets_fit(lda, ldb, sa_stride_m))
-        return DG_ERR_UNSUPPORTED;
-    switch (tile_override()) {
-    case 2: return launch_tiles<dgk::kContiguous, CfgNarrow>(p, 1, dev.cus, (hipStream_t)stream);
-    case 3: return launch_tiles<dgk::kContiguous, CfgWide>(p, 1, dev.cus, (hipStream_t)stream);
-    case 4: return launch_tiles<dgk::kContiguous, CfgDense>(p, 1, dev.cus, (hipStream_t)stream);
-    default:
-        if (N % 256 == 0)
-            return launch_tiles<dgk::kContiguous, CfgBig>(p, 1, dev.cus, (hipStream_t)stream);
-        return launch_tiles<dgk::kContiguous, CfgDense>(p, 1, dev.cus, (hipStream_t)stream);
-    }
+int dg_fp8_grouped_gemm_contiguous_to_tokens(const void *A, int64_t lda, const float *sA, int64_t sa_stride_m,
+                                             int64_t sa_stride_kb, const void *B, int64_t ldb, int64_t b_stride_g,
+                                             const float *sB, int64_t sb_stride_g, int64_t sb_stride_nb,
+                                             int64_t sb_stride_kb, const int32_t *expert_ids,
+                                             const int32_t *token_of_row, void *out, int64_t ldo, int64_t T,
+                                             int64_t M_total, int64_t N, int64_t K, int64_t G, void *stream)
+{
+    if (M_total > 0 && N > 0 && G > 0 && T > 0 && !token_of_row)
+        return DG_ERR_NULL_POINTER;
+    return contiguous_impl(A, lda, sA, sa_stride_m, sa_stride_kb, B, ldb, b_stride_g, sB, sb_stride_g,
+                           sb_stride_nb, sb_stride_kb, expert_ids, token_of_row, out, ldo, T, M_total, N, K, G,
+                           stream);
 }
 
 int dg_fp8_grouped_gemm_masked(const void *A, int64_t lda, int64_t a_stride_g, const float *sA, int64_t sa_stride_g,

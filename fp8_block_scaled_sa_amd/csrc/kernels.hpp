@@ -58,6 +58,10 @@ struct Params {
     // adds them in slice order. ksplit <= 1: no split, bf16 written directly.
     int ksplit;
     float *ws;
+    // Contiguous layout written straight to token order: row m of the
+    // result goes to row row_dst[m] of D, for 0 <= row_dst[m] < dst_rows.
+    const int32_t *row_dst;
+    int dst_rows;
 };
 
 // One e4m3 x e4m3 -> fp32 MFMA over a 16x16x128 block, C = 0 + A.B.
@@ -296,7 +300,7 @@ __device__ __forceinline__ void wait_stage(int per_stage)
         wait_vmcnt<(SEGW + 2) * LATER>();
 }
 
-template <int L, class C, int F = 0>
+template <int L, class C, int F = 0, bool SCATTER = false>
 __global__ void __launch_bounds__(C::kThreads, 1) tile_kernel(Params p)
 {
     constexpr int BM = C::kBM, BN = C::kBN, S = C::kStages;
@@ -591,7 +595,14 @@ __global__ void __launch_bounds__(C::kThreads, 1) tile_kernel(Params p)
                 const int m = m0 + wm0 + 16 * i + l16;
                 if (!row_ok(m))
                     continue;
-                uint16_t *drow = Dg + (int64_t)m * p.ldd + n0 + wn0 + 4 * lg;
+                int64_t dm = m;
+                if constexpr (SCATTER) {  // the row's token: its row of D in token order
+                    const int t = p.row_dst[m];
+                    if (t < 0 || t >= p.dst_rows)
+                        continue;
+                    dm = t;
+                }
+                uint16_t *drow = Dg + dm * p.ldd + n0 + wn0 + 4 * lg;
 #pragma unroll
                 for (int j = 0; j < NJ; ++j)
                     *reinterpret_cast<uint2 *>(drow + 16 * j) = pack_bf16x4(acc[i][j]);

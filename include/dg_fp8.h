@@ -168,6 +168,28 @@ int dg_fp8_grouped_gemm_contiguous(const void *A, int64_t lda,
                                    int64_t M_total, int64_t N, int64_t K, int64_t G, void *stream);
 
 /*
+ * The contiguous grouped GEMM written straight to token order: row r of the
+ * result (a row dg_fp8_grouped_gemm_contiguous would write) goes to row
+ * token_of_row[r] of out instead of row r of D, when 0 <= token_of_row[r] < T.
+ * This folds dg_moe_unpermute into the GEMM's epilogue.
+ *   token_of_row [M_total] int32 (device), as written by dg_moe_route_contiguous
+ *   out [T, N] bf16, row stride ldo: rows of tokens that no row names (dropped
+ *   tokens) are NOT written.
+ * Precondition: no token appears twice in token_of_row (the routing call
+ * guarantees it); otherwise which row lands last is unspecified.
+ * Other arguments, constraints and errors as dg_fp8_grouped_gemm_contiguous,
+ * with out/ldo/T in place of D/ldd/M_total for the output.
+ */
+int dg_fp8_grouped_gemm_contiguous_to_tokens(const void *A, int64_t lda,
+                                             const float *sA, int64_t sa_stride_m, int64_t sa_stride_kb,
+                                             const void *B, int64_t ldb, int64_t b_stride_g,
+                                             const float *sB, int64_t sb_stride_g, int64_t sb_stride_nb,
+                                             int64_t sb_stride_kb,
+                                             const int32_t *expert_ids, const int32_t *token_of_row,
+                                             void *out, int64_t ldo, int64_t T,
+                                             int64_t M_total, int64_t N, int64_t K, int64_t G, void *stream);
+
+/*
  * Grouped GEMM, masked layout (MoE decode): every expert owns a fixed block
  * of M_max rows and masked_m[g] (device memory, read by the kernel, so the
  * call needs no host synchronisation and the counts may change between

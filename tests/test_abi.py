@@ -291,3 +291,27 @@ def test_fmt_validation(kw, status):
 
 def test_fmt_empty():
     assert nt_fmt(M=0) == DG_OK and nt_fmt(a_fmt=1, b_fmt=1, N=0) == DG_OK
+
+
+def contig_tokens(**kw):
+    args = dict(A=A, lda=512, sA=SA, sa_m=1, sa_kb=256, B=B, ldb=512, b_stride_g=256 * 512,
+                sB=SB, sb_g=8, sb_nb=4, sb_kb=1, ids=IDS, tok=E, out=D, ldo=256, T=200,
+                M_total=256, N=256, K=512, G=4, stream=None)
+    args.update(kw)
+    return _lib.load().dg_fp8_grouped_gemm_contiguous_to_tokens(*args.values())
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(tok=None), DG_ERR_NULL_POINTER),
+    (dict(tok=E + 2), DG_ERR_MISALIGNED),
+    (dict(T=-1), DG_ERR_BAD_SHAPE),
+    (dict(M_total=200), DG_ERR_BAD_SHAPE),
+    (dict(out=E), DG_ERR_ALIASING),
+    (dict(ldo=128), DG_ERR_BAD_STRIDE),
+])
+def test_contiguous_to_tokens_validation(kw, status):
+    assert contig_tokens(**kw) == status
+
+
+def test_contiguous_to_tokens_empty():
+    assert contig_tokens(T=0) == DG_OK and contig_tokens(M_total=0, tok=None) == DG_OK

@@ -12,8 +12,8 @@ import torch
 import oracle
 from fp8_block_scaled_sa_amd import ops
 from synth import gen
-from tests.check import assert_close
-from tests.gpu_util import bits, dev
+from tests.check import SENTINEL, assert_close
+from tests.gpu_util import bits, dev, sentinel_bf16
 
 pytestmark = pytest.mark.gpu
 
@@ -100,8 +100,33 @@ def moe_step_gpu(x, e, b, sb, G):
     q, s = ops.dg_fp8_quantize_1x128_gather(xd, tok)
     d = ops.dg_fp8_grouped_gemm_contiguous(q, s, dev(b), dev(sb), ids)
     out = ops.dg_moe_unpermute(d, row)
+    fused = torch.zeros_like(out)                  # dropped tokens: zeros, as the un-permute writes
+    ops.dg_fp8_grouped_gemm_contiguous_to_tokens(q, s, dev(b), dev(sb), ids, tok, x.shape[0], out=fused)
     torch.cuda.synchronize()
+    assert torch.equal(fused.view(torch.int16), out.view(torch.int16)), "fused epilogue differs from GEMM + un-permute"
     return out, row.cpu().numpy(), ids.cpu().numpy(), tok.cpu().numpy(), q.cpu().numpy(), s.cpu().numpy()
+
+
+def test_to_tokens_equals_gemm_then_unpermute(gpu_device):
+    """The GEMM written straight to token order equals the GEMM followed by
+    the un-permute bit for bit; rows of dropped tokens stay untouched."""
+    T, G, N, K = 700, 5, 384, 1024
+    x = torch.from_numpy(gen.normal_with_outliers(np.random.Generator(np.random.PCG64(931)), (T, K)))
+    e = np.random.Generator(np.random.PCG64(932)).choice(G, T).astype(np.int32)
+    e[::11] = -1
+    b, sb = gen.make_grouped_rhs(G, N, K, 933)
+    bd, sbd = dev(b), dev(sb)
+    row, ids, tok, _ = ops.dg_moe_route_contiguous(dev(e), G)
+    q, s = ops.dg_fp8_quantize_1x128_gather(x.cuda(), tok)
+    d = ops.dg_fp8_grouped_gemm_contiguous(q, s, bd, sbd, ids)
+    ref = ops.dg_moe_unpermute(d, row)
+    out = sentinel_bf16((T, N))
+    ops.dg_fp8_grouped_gemm_contiguous_to_tokens(q, s, bd, sbd, ids, tok, T, out=out)
+    torch.cuda.synchronize()
+    got, want = bits(out), bits(ref)
+    kept = e >= 0
+    assert np.array_equal(got[kept], want[kept])
+    assert np.all(got[~kept] == SENTINEL)
 
 
 def test_moe_step_small_full_parity(gpu_device):
