@@ -1,6 +1,7 @@
 """HIP-graph capture and replay through the C ABI.
 
-The masked layout reads its per-group valid-row counts from device memory, so
+The masked layout reads its per-group valid-row counts from device memory, and
+the MoE routing step keeps its sizes on the device as well, so
 one captured launch serves any counts (bhfrc.com DeepGEMM article, §4.3: shape
 data kept in device memory avoids rebuilding the launch). Each test captures
 once, then changes the inputs between replays, with eager work and
@@ -136,3 +137,68 @@ def test_masked_full_size_graph_replay(gpu_device):
         ref, _, produced = oracle.grouped_masked_points(p.a, p.sa_t, p.b, p.sb, counts, gs, ms, ns)
         sel = produced
         assert_close(got[gs[sel], ms[sel], ns[sel]], ref[sel], "full-size replay")
+
+
+def test_moe_step_graph_replay_with_changing_routing(gpu_device):
+    """Routing, quantisation into the layout and the grouped GEMM to token
+    order captured once; new routings and activations are copied into the
+    captured buffers between replays. Nothing in the step reads sizes on the
+    host, so every replay must equal the eager chain bit for bit."""
+    T, G, N, K = 500, 6, 256, 512
+    b, sb = gen.make_grouped_rhs(G, N, K, 821)
+    bd, sbd = dev(b), dev(sb)
+    M_cap = ops.dg_moe_contiguous_max_rows(T, G)
+    e_buf = torch.zeros(T, dtype=torch.int32, device="cuda")
+    x = torch.zeros((T, K), dtype=torch.bfloat16, device="cuda")
+    row = torch.empty(T, dtype=torch.int32, device="cuda")
+    ids = torch.empty(M_cap, dtype=torch.int32, device="cuda")
+    tok = torch.empty(M_cap, dtype=torch.int32, device="cuda")
+    layout = torch.empty(G + 1, dtype=torch.int32, device="cuda")
+    q = torch.empty((M_cap, K), dtype=torch.uint8, device="cuda")
+    s = torch.empty((K // 128, M_cap), dtype=torch.float32, device="cuda").t()
+    out = torch.empty((T, N), dtype=torch.bfloat16, device="cuda")
+    lib = ops._lib.load()
+
+    def step():
+        st = lib.dg_moe_route_contiguous(e_buf.data_ptr(), T, G, row.data_ptr(), ids.data_ptr(), tok.data_ptr(),
+                                         layout.data_ptr(), M_cap, torch.cuda.current_stream().cuda_stream)
+        assert st == 0
+        ops.dg_fp8_quantize_1x128_gather(x, tok, q=q, s=s)
+        ops.dg_fp8_grouped_gemm_contiguous_to_tokens(q, s, bd, sbd, ids, tok, T, out=out)
+
+    stream = torch.cuda.Stream()
+    stream.wait_stream(torch.cuda.current_stream())
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=stream):
+        step()
+    torch.cuda.synchronize()
+    for seed in (822, 823, 824):
+        rng = np.random.Generator(np.random.PCG64(seed))
+        e = rng.choice(G, T).astype(np.int32)
+        e[rng.random(T) < 0.05] = -1                      # a few dropped tokens
+        if seed == 823:
+            e[:] = 2                                      # everything to one expert
+        xb = torch.from_numpy(gen.normal_with_outliers(rng, (T, K))).to(torch.bfloat16)
+        e_buf.copy_(torch.from_numpy(e))
+        x.copy_(xb)
+        out.view(torch.int16).fill_(SENTINEL)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        got = bits(out)
+        r_row, r_ids, r_tok, r_layout = oracle.moe_route_contiguous(e, G, M_cap=M_cap)
+        assert np.array_equal(row.cpu().numpy(), r_row) and np.array_equal(ids.cpu().numpy(), r_ids)
+        assert np.array_equal(layout.cpu().numpy(), r_layout)
+        out.view(torch.int16).fill_(SENTINEL)
+        step()                                            # the same step, eager
+        torch.cuda.synchronize()
+        assert np.array_equal(got, bits(out)), "replay differs from the eager step (seed %d)" % seed
+        kept = e >= 0
+        assert np.all(got[~kept] == SENTINEL)
+        xh = xb.view(torch.int16).numpy().view(np.uint16)
+        rq, rs = oracle.quantize_1x128(xh[kept])
+        ns = np.tile(np.arange(0, N, 37), kept.sum())
+        rows = np.repeat(np.arange(kept.sum()), len(np.arange(0, N, 37)))
+        ref, _, produced = oracle.grouped_contiguous_points(rq, rs, b, sb, e[kept], rows, ns)
+        assert produced.all()
+        assert_close(got[np.nonzero(kept)[0][rows], ns], ref, "MoE step replay, seed %d" % seed)
