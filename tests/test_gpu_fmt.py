@@ -58,3 +58,34 @@ def test_fmt_square_4096_sampled(gpu_device):
     ref, _ = oracle.gemm_nt_fmt_points(p.a, "e4m3", p.sa_t.T, p.b, "e5m2", p.sb, ms, ns)
     assert_close(got[ms, ns], ref, "4096^3 e4m3 x e5m2")
     assert not np.any(got == 0x7FA5)      # every output written
+
+
+@pytest.mark.parametrize("side", ["A", "B"])
+def test_mfma_decodes_every_e5m2_code(gpu_device, side):
+    """Every finite e5m2 code through the MFMA, in either operand position:
+    the code row times an identity (1.0 on the diagonal, the other format) with
+    unit scales gives the decoded value, exact in bf16 (3 significant bits,
+    exponents 2^-16 .. 2^15)."""
+    codes = np.array([c for c in range(256) if (c & 0x7C) != 0x7C], np.uint8)    # 248 finite codes
+    K = 256
+    vals = np.zeros((2, K), np.uint8)
+    vals.ravel()[:len(codes)] = codes                    # two rows of up to 256 codes (K positions)
+    ident_e4m3 = np.zeros((K, K), np.uint8)
+    np.fill_diagonal(ident_e4m3, 0x38)
+    ones = lambda r, c: np.ones((r, c), np.float32)      # noqa: E731
+    d = sentinel_bf16((2, K))
+    if side == "A":    # A holds e5m2 codes, B = I in e4m3: D = dec_e5m2(A)
+        ops.dg_fp8_gemm_nt_fmt(dev(vals), dev(ones(2, 2)), dev(ident_e4m3), dev(ones(2, 2)), "e5m2", "e4m3", d=d)
+    else:              # B holds e5m2 codes, A = I in e4m3: D[m, n] = dec_e5m2(B[n, m]) -> the codes come out on a row
+        b = np.zeros((K, K), np.uint8)
+        b[:, :2] = vals.T                                # B[n, m] = vals[m, n]
+        ident_rows = np.zeros((2, K), np.uint8)
+        ident_rows[0, 0] = ident_rows[1, 1] = 0x38
+        ops.dg_fp8_gemm_nt_fmt(dev(ident_rows), dev(ones(2, 2)), dev(b), dev(ones(2, 2)), "e4m3", "e5m2", d=d)
+    torch.cuda.synchronize()
+    got = bits(d).ravel()[:len(codes)]
+    want = torch.from_numpy(codes).view(torch.float8_e5m2).to(torch.float32).to(torch.bfloat16)
+    want = want.view(torch.int16).numpy().view(np.uint16)
+    nz = (codes & 0x7F) != 0          # -0 sums with +0 products to +0: zeros compare by value
+    assert np.array_equal(got[nz], want[nz])
+    assert np.all((got[~nz] & 0x7FFF) == 0)
