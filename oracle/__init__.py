@@ -36,33 +36,43 @@ def build(force: bool = False) -> str:
 _lib = None
 
 
+def configure(cdll):
+    """Set the return and argument types of an oracle library (also used by
+    the tests that load copies of the oracle with planted mistakes)."""
+    _lib_setup(cdll)
+    return cdll
+
+
 def lib():
     global _lib
     if _lib is None:
-        _lib = ctypes.CDLL(build())
-        _lib.dgo_e4m3_decode.restype = ctypes.c_double
-        _lib.dgo_e4m3_decode.argtypes = [ctypes.c_uint8]
-        _lib.dgo_bf16_rne.restype = ctypes.c_uint16
-        _lib.dgo_bf16_rne.argtypes = [ctypes.c_double]
-        _lib.dgo_block_partial.restype = ctypes.c_double
-        _lib.dgo_block_partial.argtypes = [_p, _p]
-        _lib.dgo_max_threads.restype = ctypes.c_int
-        _lib.dgo_e4m3_encode.restype = ctypes.c_uint8
-        _lib.dgo_e4m3_encode.argtypes = [ctypes.c_float]
-        _lib.dgo_quantize_1x128.restype = None
-        _lib.dgo_moe_route_contiguous.restype = ctypes.c_int
-        _lib.dgo_e5m2_decode.restype = ctypes.c_double
-        _lib.dgo_e5m2_decode.argtypes = [ctypes.c_uint8]
-        _lib.dgo_block_partial_fmt.restype = ctypes.c_double
-        _lib.dgo_block_partial_fmt.argtypes = [_p, ctypes.c_int, _p, ctypes.c_int]
-        _lib.dgo_gemm_nt_fmt.restype = None
-        _lib.dgo_gemm_nt_fmt_points.restype = None
-        _lib.dgo_moe_unpermute.restype = None
-        for name in ("dgo_gemm_nt", "dgo_gemm_nt_points", "dgo_grouped_contiguous",
-                     "dgo_grouped_contiguous_points", "dgo_grouped_masked",
-                     "dgo_grouped_masked_points"):
-            getattr(_lib, name).restype = None
+        _lib = configure(ctypes.CDLL(build()))
     return _lib
+
+
+def _lib_setup(cdll):
+    cdll.dgo_e4m3_decode.restype = ctypes.c_double
+    cdll.dgo_e4m3_decode.argtypes = [ctypes.c_uint8]
+    cdll.dgo_bf16_rne.restype = ctypes.c_uint16
+    cdll.dgo_bf16_rne.argtypes = [ctypes.c_double]
+    cdll.dgo_block_partial.restype = ctypes.c_double
+    cdll.dgo_block_partial.argtypes = [_p, _p]
+    cdll.dgo_max_threads.restype = ctypes.c_int
+    cdll.dgo_e4m3_encode.restype = ctypes.c_uint8
+    cdll.dgo_e4m3_encode.argtypes = [ctypes.c_float]
+    cdll.dgo_quantize_1x128.restype = None
+    cdll.dgo_moe_route_contiguous.restype = ctypes.c_int
+    cdll.dgo_e5m2_decode.restype = ctypes.c_double
+    cdll.dgo_e5m2_decode.argtypes = [ctypes.c_uint8]
+    cdll.dgo_block_partial_fmt.restype = ctypes.c_double
+    cdll.dgo_block_partial_fmt.argtypes = [_p, ctypes.c_int, _p, ctypes.c_int]
+    cdll.dgo_gemm_nt_fmt.restype = None
+    cdll.dgo_gemm_nt_fmt_points.restype = None
+    cdll.dgo_moe_unpermute.restype = None
+    for name in ("dgo_gemm_nt", "dgo_gemm_nt_points", "dgo_grouped_contiguous",
+                 "dgo_grouped_contiguous_points", "dgo_grouped_masked",
+                 "dgo_grouped_masked_points"):
+        getattr(cdll, name).restype = None
 
 
 def _ptr(a: np.ndarray):
