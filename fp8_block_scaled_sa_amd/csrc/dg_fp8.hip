@@ -185,6 +185,26 @@ int launch_tiles(dgk::Params &p, int groups, int cus, hipStream_t stream)
     return e == hipSuccess ? DG_OK : fail_hip(e);
 }
 
+// launch_tiles with the operand formats chosen at run time (bit 0: A is e5m2,
+// bit 1: B is e5m2); the formats only set the MFMA's format selectors.
+template <int L, class C>
+int launch_tiles_fmt(dgk::Params &p, int groups, int cus, hipStream_t stream, int f)
+{
+    switch (f) {
+    case 1: return launch_tiles<L, C, 1>(p, groups, cus, stream);
+    case 2: return launch_tiles<L, C, 2>(p, groups, cus, stream);
+    case 3: return launch_tiles<L, C, 3>(p, groups, cus, stream);
+    default: return launch_tiles<L, C, 0>(p, groups, cus, stream);
+    }
+}
+
+int format_bits(int a_fmt, int b_fmt)
+{
+    if ((a_fmt != DG_FP8_E4M3 && a_fmt != DG_FP8_E5M2) || (b_fmt != DG_FP8_E4M3 && b_fmt != DG_FP8_E5M2))
+        return -1;
+    return (a_fmt == DG_FP8_E5M2 ? 1 : 0) | (b_fmt == DG_FP8_E5M2 ? 2 : 0);
+}
+
 // Dense GEMM on configuration C. When the tiles fill at most half of the CUs
 // (small M, or small M x N), each tile's K blocks are split over ks work items
 // (tiles * ks <= CUs, one round) that write fp32 partials; a second kernel
@@ -503,7 +523,7 @@ int contiguous_impl(const void *A, int64_t lda, const float *sA, int64_t sa_stri
                     const void *B, int64_t ldb, int64_t b_stride_g, const float *sB, int64_t sb_stride_g,
                     int64_t sb_stride_nb, int64_t sb_stride_kb, const int32_t *expert_ids,
                     const int32_t *token_of_row, void *D, int64_t ldd, int64_t d_rows, int64_t M_total, int64_t N,
-                    int64_t K, int64_t G, void *stream)
+                    int64_t K, int64_t G, void *stream, int fmt = 0)
 {
     int st = check_common_shape(M_total, N, K);
     if (st != DG_OK)
@@ -558,6 +578,11 @@ int contiguous_impl(const void *A, int64_t lda, const float *sA, int64_t sa_stri
             return launch_tiles<dgk::kContiguous, CfgBig, 0, true>(p, 1, dev.cus, (hipStream_t)stream);
         return launch_tiles<dgk::kContiguous, CfgDense, 0, true>(p, 1, dev.cus, (hipStream_t)stream);
     }
+    if (fmt) {
+        if (N % 256 == 0)
+            return launch_tiles_fmt<dgk::kContiguous, CfgBig>(p, 1, dev.cus, (hipStream_t)stream, fmt);
+        return launch_tiles_fmt<dgk::kContiguous, CfgDense>(p, 1, dev.cus, (hipStream_t)stream, fmt);
+    }
     switch (tile_override()) {
     case 2: return launch_tiles<dgk::kContiguous, CfgNarrow>(p, 1, dev.cus, (hipStream_t)stream);
     case 3: return launch_tiles<dgk::kContiguous, CfgWide>(p, 1, dev.cus, (hipStream_t)stream);
@@ -566,6 +591,73 @@ int contiguous_impl(const void *A, int64_t lda, const float *sA, int64_t sa_stri
         if (N % 256 == 0)
             return launch_tiles<dgk::kContiguous, CfgBig>(p, 1, dev.cus, (hipStream_t)stream);
         return launch_tiles<dgk::kContiguous, CfgDense>(p, 1, dev.cus, (hipStream_t)stream);
+    }
+}
+
+// The masked grouped GEMM; fmt as for launch_tiles_fmt.
+int masked_impl(const void *A, int64_t lda, int64_t a_stride_g, const float *sA, int64_t sa_stride_g,
+                int64_t sa_stride_m, int64_t sa_stride_kb, const void *B, int64_t ldb, int64_t b_stride_g,
+                const float *sB, int64_t sb_stride_g, int64_t sb_stride_nb, int64_t sb_stride_kb,
+                const int32_t *masked_m, void *D, int64_t ldd, int64_t d_stride_g, int64_t G, int64_t M_max,
+                int64_t N, int64_t K, void *stream, int fmt)
+{
+    int st = check_common_shape(M_max, N, K);
+    if (st != DG_OK)
+        return st;
+    if (G < 0)
+        return DG_ERR_BAD_SHAPE;
+    if (G > kInt32Max)
+        return DG_ERR_UNSUPPORTED;
+    if (G == 0 || M_max == 0 || N == 0)
+        return DG_OK;
+    if (!A || !sA || !B || !sB || !masked_m || !D)
+        return DG_ERR_NULL_POINTER;
+    if (lda < K || ldb < K || ldd < N || sa_stride_m < 0 || sa_stride_kb < 0 || sa_stride_g < 0 ||
+        sb_stride_nb < 0 || sb_stride_kb < 0 || sb_stride_g < 0 ||
+        (G > 1 && (a_stride_g < (M_max - 1) * lda + K || b_stride_g < (N - 1) * ldb + K ||
+                   d_stride_g < (M_max - 1) * ldd + N)))
+        return DG_ERR_BAD_STRIDE;
+    if (!aligned(A, 16) || !aligned(B, 16) || !aligned(D, 16) || lda % 16 || ldb % 16 || a_stride_g % 16 ||
+        b_stride_g % 16 || ldd % 8 || d_stride_g % 8 || !aligned(sA, 4) || !aligned(sB, 4) ||
+        !aligned(masked_m, 4))
+        return DG_ERR_MISALIGNED;
+    const int64_t nkb = K / 128;
+    const Extent ed = extent(D, 2, (G - 1) * d_stride_g + (M_max - 1) * ldd + N - 1);
+    if (overlaps(ed, extent(A, 1, (G - 1) * a_stride_g + (M_max - 1) * lda + K - 1)) ||
+        overlaps(ed, extent(B, 1, (G - 1) * b_stride_g + (N - 1) * ldb + K - 1)) ||
+        overlaps(ed, extent(sA, 4, (G - 1) * sa_stride_g + last_scale_index(M_max, nkb, sa_stride_m, sa_stride_kb))) ||
+        overlaps(ed, extent(sB, 4, (G - 1) * sb_stride_g + last_scale_index(N / 128, nkb, sb_stride_nb, sb_stride_kb))) ||
+        overlaps(ed, extent(masked_m, 4, G - 1)))
+        return DG_ERR_ALIASING;
+    DeviceInfo dev;
+    if ((st = current_device(dev)) != DG_OK)
+        return st;
+
+    dgk::Params p = {};
+    p.A = (const uint8_t *)A; p.lda = lda; p.a_stride_g = a_stride_g;
+    p.sA = sA; p.sa_m = sa_stride_m; p.sa_kb = sa_stride_kb; p.sa_g = sa_stride_g;
+    p.B = (const uint8_t *)B; p.ldb = ldb; p.b_stride_g = b_stride_g;
+    p.sB = sB; p.sb_nb = sb_stride_nb; p.sb_kb = sb_stride_kb; p.sb_g = sb_stride_g;
+    p.D = (uint16_t *)D; p.ldd = ldd; p.d_stride_g = d_stride_g;
+    p.masked_m = masked_m;
+    p.M = (int)M_max; p.N = (int)N; p.K = (int)K; p.G = (int)G;
+    if (!offsets_fit(lda, ldb, sa_stride_m))
+        return DG_ERR_UNSUPPORTED;
+    if (fmt) {
+        if (N % 256 == 0)
+            return launch_tiles_fmt<dgk::kMasked, CfgBigStreamB>(p, (int)G, dev.cus, (hipStream_t)stream, fmt);
+        return launch_tiles_fmt<dgk::kMasked, CfgDense>(p, (int)G, dev.cus, (hipStream_t)stream, fmt);
+    }
+    switch (tile_override()) {
+    case 1: return launch_tiles<dgk::kMasked, CfgDense4>(p, (int)G, dev.cus, (hipStream_t)stream);
+    case 2: return launch_tiles<dgk::kMasked, CfgNarrow>(p, (int)G, dev.cus, (hipStream_t)stream);
+    case 4: return launch_tiles<dgk::kMasked, CfgDense>(p, (int)G, dev.cus, (hipStream_t)stream);
+    case 12: return N % 256 == 0 ? launch_tiles<dgk::kMasked, CfgBig>(p, (int)G, dev.cus, (hipStream_t)stream)
+                                 : DG_ERR_UNSUPPORTED;
+    default:
+        if (N % 256 == 0)
+            return launch_tiles<dgk::kMasked, CfgBigStreamB>(p, (int)G, dev.cus, (hipStream_t)stream);
+        return launch_tiles<dgk::kMasked, CfgDense>(p, (int)G, dev.cus, (hipStream_t)stream);
     }
 }
 
@@ -660,59 +752,39 @@ int dg_fp8_grouped_gemm_masked(const void *A, int64_t lda, int64_t a_stride_g, c
                                int64_t sb_stride_kb, const int32_t *masked_m, void *D, int64_t ldd,
                                int64_t d_stride_g, int64_t G, int64_t M_max, int64_t N, int64_t K, void *stream)
 {
-    int st = check_common_shape(M_max, N, K);
-    if (st != DG_OK)
-        return st;
-    if (G < 0)
-        return DG_ERR_BAD_SHAPE;
-    if (G > kInt32Max)
-        return DG_ERR_UNSUPPORTED;
-    if (G == 0 || M_max == 0 || N == 0)
-        return DG_OK;
-    if (!A || !sA || !B || !sB || !masked_m || !D)
-        return DG_ERR_NULL_POINTER;
-    if (lda < K || ldb < K || ldd < N || sa_stride_m < 0 || sa_stride_kb < 0 || sa_stride_g < 0 ||
-        sb_stride_nb < 0 || sb_stride_kb < 0 || sb_stride_g < 0 ||
-        (G > 1 && (a_stride_g < (M_max - 1) * lda + K || b_stride_g < (N - 1) * ldb + K ||
-                   d_stride_g < (M_max - 1) * ldd + N)))
-        return DG_ERR_BAD_STRIDE;
-    if (!aligned(A, 16) || !aligned(B, 16) || !aligned(D, 16) || lda % 16 || ldb % 16 || a_stride_g % 16 ||
-        b_stride_g % 16 || ldd % 8 || d_stride_g % 8 || !aligned(sA, 4) || !aligned(sB, 4) ||
-        !aligned(masked_m, 4))
-        return DG_ERR_MISALIGNED;
-    const int64_t nkb = K / 128;
-    const Extent ed = extent(D, 2, (G - 1) * d_stride_g + (M_max - 1) * ldd + N - 1);
-    if (overlaps(ed, extent(A, 1, (G - 1) * a_stride_g + (M_max - 1) * lda + K - 1)) ||
-        overlaps(ed, extent(B, 1, (G - 1) * b_stride_g + (N - 1) * ldb + K - 1)) ||
-        overlaps(ed, extent(sA, 4, (G - 1) * sa_stride_g + last_scale_index(M_max, nkb, sa_stride_m, sa_stride_kb))) ||
-        overlaps(ed, extent(sB, 4, (G - 1) * sb_stride_g + last_scale_index(N / 128, nkb, sb_stride_nb, sb_stride_kb))) ||
-        overlaps(ed, extent(masked_m, 4, G - 1)))
-        return DG_ERR_ALIASING;
-    DeviceInfo dev;
-    if ((st = current_device(dev)) != DG_OK)
-        return st;
+    return masked_impl(A, lda, a_stride_g, sA, sa_stride_g, sa_stride_m, sa_stride_kb, B, ldb, b_stride_g, sB,
+                       sb_stride_g, sb_stride_nb, sb_stride_kb, masked_m, D, ldd, d_stride_g, G, M_max, N, K, stream,
+                       0);
+}
 
-    dgk::Params p = {};
-    p.A = (const uint8_t *)A; p.lda = lda; p.a_stride_g = a_stride_g;
-    p.sA = sA; p.sa_m = sa_stride_m; p.sa_kb = sa_stride_kb; p.sa_g = sa_stride_g;
-    p.B = (const uint8_t *)B; p.ldb = ldb; p.b_stride_g = b_stride_g;
-    p.sB = sB; p.sb_nb = sb_stride_nb; p.sb_kb = sb_stride_kb; p.sb_g = sb_stride_g;
-    p.D = (uint16_t *)D; p.ldd = ldd; p.d_stride_g = d_stride_g;
-    p.masked_m = masked_m;
-    p.M = (int)M_max; p.N = (int)N; p.K = (int)K; p.G = (int)G;
-    if (!offsets_fit(lda, ldb, sa_stride_m))
+int dg_fp8_grouped_gemm_masked_fmt(const void *A, int a_fmt, int64_t lda, int64_t a_stride_g, const float *sA,
+                                   int64_t sa_stride_g, int64_t sa_stride_m, int64_t sa_stride_kb, const void *B,
+                                   int b_fmt, int64_t ldb, int64_t b_stride_g, const float *sB, int64_t sb_stride_g,
+                                   int64_t sb_stride_nb, int64_t sb_stride_kb, const int32_t *masked_m, void *D,
+                                   int64_t ldd, int64_t d_stride_g, int64_t G, int64_t M_max, int64_t N, int64_t K,
+                                   void *stream)
+{
+    const int f = format_bits(a_fmt, b_fmt);
+    if (f < 0)
         return DG_ERR_UNSUPPORTED;
-    switch (tile_override()) {
-    case 1: return launch_tiles<dgk::kMasked, CfgDense4>(p, (int)G, dev.cus, (hipStream_t)stream);
-    case 2: return launch_tiles<dgk::kMasked, CfgNarrow>(p, (int)G, dev.cus, (hipStream_t)stream);
-    case 4: return launch_tiles<dgk::kMasked, CfgDense>(p, (int)G, dev.cus, (hipStream_t)stream);
-    case 12: return N % 256 == 0 ? launch_tiles<dgk::kMasked, CfgBig>(p, (int)G, dev.cus, (hipStream_t)stream)
-                                 : DG_ERR_UNSUPPORTED;
-    default:
-        if (N % 256 == 0)
-            return launch_tiles<dgk::kMasked, CfgBigStreamB>(p, (int)G, dev.cus, (hipStream_t)stream);
-        return launch_tiles<dgk::kMasked, CfgDense>(p, (int)G, dev.cus, (hipStream_t)stream);
-    }
+    return masked_impl(A, lda, a_stride_g, sA, sa_stride_g, sa_stride_m, sa_stride_kb, B, ldb, b_stride_g, sB,
+                       sb_stride_g, sb_stride_nb, sb_stride_kb, masked_m, D, ldd, d_stride_g, G, M_max, N, K, stream,
+                       f);
+}
+
+int dg_fp8_grouped_gemm_contiguous_fmt(const void *A, int a_fmt, int64_t lda, const float *sA, int64_t sa_stride_m,
+                                       int64_t sa_stride_kb, const void *B, int b_fmt, int64_t ldb,
+                                       int64_t b_stride_g, const float *sB, int64_t sb_stride_g,
+                                       int64_t sb_stride_nb, int64_t sb_stride_kb, const int32_t *expert_ids,
+                                       void *D, int64_t ldd, int64_t M_total, int64_t N, int64_t K, int64_t G,
+                                       void *stream)
+{
+    const int f = format_bits(a_fmt, b_fmt);
+    if (f < 0)
+        return DG_ERR_UNSUPPORTED;
+    return contiguous_impl(A, lda, sA, sa_stride_m, sa_stride_kb, B, ldb, b_stride_g, sB, sb_stride_g,
+                           sb_stride_nb, sb_stride_kb, expert_ids, nullptr, D, ldd, M_total, M_total, N, K, G,
+                           stream, f);
 }
 
 int dg_fp8_gemm_nt_fmt(const void *A, int a_fmt, int64_t lda, const float *sA, int64_t sa_stride_m,

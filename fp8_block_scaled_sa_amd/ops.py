@@ -287,3 +287,41 @@ def dg_moe_unpermute(d, row_of_token, out=None, stream=None):
                               _dev_or_null(out, "out"), out.stride(0), _stream(stream))
     _check(st, "dg_moe_unpermute")
     return out
+
+
+def _fmt_codes(t, name, ndim):
+    if t.dtype not in (torch.uint8, torch.float8_e4m3fn, torch.float8_e5m2) or t.dim() != ndim or t.stride(-1) != 1:
+        raise TypeError("%s must be a %d-D fp8 code tensor with a contiguous last (K) dimension" % (name, ndim))
+
+
+def dg_fp8_grouped_gemm_contiguous_fmt(a, sa, b, sb, expert_ids, a_fmt="e4m3", b_fmt="e4m3", d=None, stream=None):
+    """dg_fp8_grouped_gemm_contiguous with a per-operand fp8 format ("e4m3" or "e5m2")."""
+    _fmt_codes(a, "a", 2), _fmt_codes(b, "b", 3), _scales(sa, "sa", 2), _scales(sb, "sb", 3)
+    M_total, K = a.shape
+    G, N, _ = b.shape
+    if d is None:
+        d = torch.empty((M_total, N), dtype=torch.bfloat16, device=a.device)
+    lib = _lib.load()
+    st = lib.dg_fp8_grouped_gemm_contiguous_fmt(
+        _dev(a, "a"), FORMATS[a_fmt], a.stride(0), _dev(sa, "sa"), sa.stride(0), sa.stride(1),
+        _dev(b, "b"), FORMATS[b_fmt], b.stride(1), b.stride(0), _dev(sb, "sb"), sb.stride(0), sb.stride(1),
+        sb.stride(2), _dev(expert_ids, "expert_ids"), _dev(d, "d"), d.stride(0), M_total, N, K, G, _stream(stream))
+    _check(st, "dg_fp8_grouped_gemm_contiguous_fmt")
+    return d
+
+
+def dg_fp8_grouped_gemm_masked_fmt(a, sa, b, sb, masked_m, a_fmt="e4m3", b_fmt="e4m3", d=None, stream=None):
+    """dg_fp8_grouped_gemm_masked with a per-operand fp8 format ("e4m3" or "e5m2")."""
+    _fmt_codes(a, "a", 3), _fmt_codes(b, "b", 3), _scales(sa, "sa", 3), _scales(sb, "sb", 3)
+    G, M_max, K = a.shape
+    N = b.shape[1]
+    if d is None:
+        d = torch.empty((G, M_max, N), dtype=torch.bfloat16, device=a.device)
+    lib = _lib.load()
+    st = lib.dg_fp8_grouped_gemm_masked_fmt(
+        _dev(a, "a"), FORMATS[a_fmt], a.stride(1), a.stride(0), _dev(sa, "sa"), sa.stride(0), sa.stride(1),
+        sa.stride(2), _dev(b, "b"), FORMATS[b_fmt], b.stride(1), b.stride(0), _dev(sb, "sb"), sb.stride(0),
+        sb.stride(1), sb.stride(2), _dev(masked_m, "masked_m"), _dev(d, "d"), d.stride(1), d.stride(0),
+        G, M_max, N, K, _stream(stream))
+    _check(st, "dg_fp8_grouped_gemm_masked_fmt")
+    return d

@@ -190,6 +190,20 @@ int dg_fp8_grouped_gemm_contiguous_to_tokens(const void *A, int64_t lda,
                                              int64_t M_total, int64_t N, int64_t K, int64_t G, void *stream);
 
 /*
+ * The contiguous grouped GEMM with a choice of fp8 format per operand
+ * (a_fmt / b_fmt: DG_FP8_E4M3 or DG_FP8_E5M2, as in dg_fp8_gemm_nt_fmt);
+ * otherwise identical to dg_fp8_grouped_gemm_contiguous.
+ */
+int dg_fp8_grouped_gemm_contiguous_fmt(const void *A, int a_fmt, int64_t lda,
+                                       const float *sA, int64_t sa_stride_m, int64_t sa_stride_kb,
+                                       const void *B, int b_fmt, int64_t ldb, int64_t b_stride_g,
+                                       const float *sB, int64_t sb_stride_g, int64_t sb_stride_nb,
+                                       int64_t sb_stride_kb,
+                                       const int32_t *expert_ids,
+                                       void *D, int64_t ldd,
+                                       int64_t M_total, int64_t N, int64_t K, int64_t G, void *stream);
+
+/*
  * Grouped GEMM, masked layout (MoE decode): every expert owns a fixed block
  * of M_max rows and masked_m[g] (device memory, read by the kernel, so the
  * call needs no host synchronisation and the counts may change between
@@ -212,6 +226,21 @@ int dg_fp8_grouped_gemm_masked(const void *A, int64_t lda, int64_t a_stride_g,
                                const int32_t *masked_m,
                                void *D, int64_t ldd, int64_t d_stride_g,
                                int64_t G, int64_t M_max, int64_t N, int64_t K, void *stream);
+
+/*
+ * The masked grouped GEMM with a choice of fp8 format per operand (a_fmt /
+ * b_fmt: DG_FP8_E4M3 or DG_FP8_E5M2, as in dg_fp8_gemm_nt_fmt); otherwise
+ * identical to dg_fp8_grouped_gemm_masked.
+ */
+int dg_fp8_grouped_gemm_masked_fmt(const void *A, int a_fmt, int64_t lda, int64_t a_stride_g,
+                                   const float *sA, int64_t sa_stride_g, int64_t sa_stride_m,
+                                   int64_t sa_stride_kb,
+                                   const void *B, int b_fmt, int64_t ldb, int64_t b_stride_g,
+                                   const float *sB, int64_t sb_stride_g, int64_t sb_stride_nb,
+                                   int64_t sb_stride_kb,
+                                   const int32_t *masked_m,
+                                   void *D, int64_t ldd, int64_t d_stride_g,
+                                   int64_t G, int64_t M_max, int64_t N, int64_t K, void *stream);
 
 /* Element types of the quantiser's input. */
 #define DG_DTYPE_F32 0

@@ -315,3 +315,37 @@ def test_contiguous_to_tokens_validation(kw, status):
 
 def test_contiguous_to_tokens_empty():
     assert contig_tokens(T=0) == DG_OK and contig_tokens(M_total=0, tok=None) == DG_OK
+
+
+def contig_fmt(a_fmt=1, b_fmt=1, **kw):
+    args = dict(A=A, a_fmt=a_fmt, lda=512, sA=SA, sa_m=1, sa_kb=256, B=B, b_fmt=b_fmt, ldb=512,
+                b_stride_g=256 * 512, sB=SB, sb_g=8, sb_nb=4, sb_kb=1, ids=IDS, D=D, ldd=256,
+                M_total=256, N=256, K=512, G=4, stream=None)
+    args.update(kw)
+    return _lib.load().dg_fp8_grouped_gemm_contiguous_fmt(*args.values())
+
+
+def masked_fmt(a_fmt=1, b_fmt=0, **kw):
+    args = dict(A=A, a_fmt=a_fmt, lda=512, a_stride_g=64 * 512, sA=SA, sa_g=256, sa_m=1, sa_kb=64,
+                B=B, b_fmt=b_fmt, ldb=512, b_stride_g=256 * 512, sB=SB, sb_g=8, sb_nb=4, sb_kb=1,
+                masked_m=IDS, D=D, ldd=256, d_stride_g=64 * 256, G=4, M_max=64, N=256, K=512, stream=None)
+    args.update(kw)
+    return _lib.load().dg_fp8_grouped_gemm_masked_fmt(*args.values())
+
+
+@pytest.mark.parametrize("fn,kw,status", [
+    (contig_fmt, dict(a_fmt=3), DG_ERR_UNSUPPORTED),
+    (contig_fmt, dict(M_total=200), DG_ERR_BAD_SHAPE),
+    (contig_fmt, dict(ids=None), DG_ERR_NULL_POINTER),
+    (contig_fmt, dict(D=IDS), DG_ERR_ALIASING),
+    (masked_fmt, dict(b_fmt=7), DG_ERR_UNSUPPORTED),
+    (masked_fmt, dict(masked_m=None), DG_ERR_NULL_POINTER),
+    (masked_fmt, dict(d_stride_g=256), DG_ERR_BAD_STRIDE),
+    (masked_fmt, dict(D=B + 4096), DG_ERR_ALIASING),
+])
+def test_grouped_fmt_validation(fn, kw, status):
+    assert fn(**kw) == status
+
+
+def test_grouped_fmt_empty():
+    assert contig_fmt(M_total=0) == DG_OK and masked_fmt(G=0) == DG_OK

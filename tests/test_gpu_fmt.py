@@ -7,7 +7,7 @@ import torch
 import oracle
 from fp8_block_scaled_sa_amd import ops
 from synth import gen
-from tests.check import assert_close
+from tests.check import SENTINEL, assert_close
 from tests.gpu_util import bits, dev, run_dense, sentinel_bf16
 
 pytestmark = pytest.mark.gpu
@@ -89,3 +89,57 @@ def test_mfma_decodes_every_e5m2_code(gpu_device, side):
     nz = (codes & 0x7F) != 0          # -0 sums with +0 products to +0: zeros compare by value
     assert np.array_equal(got[nz], want[nz])
     assert np.all((got[~nz] & 0x7FFF) == 0)
+
+
+@pytest.mark.parametrize("fa,fb", FMT_CASES)
+def test_contiguous_fmt_matches_per_expert_dense_oracle(gpu_device, fa, fb):
+    """Contiguous layout with e5m2 operands: every routed row equals the
+    format oracle's dense GEMM of that row against its expert's B; padding rows
+    stay untouched."""
+    G, T, N, K = 5, 600, 384, 768
+    rng = np.random.default_rng(41)
+    e = rng.choice(G, T, p=rng.dirichlet(np.ones(G))).astype(np.int32)
+    ids, tok, _ = gen.route_contiguous(e, G)
+    xa, sa_tok = gen.make_lhs(T, K, 42, fa)
+    a = np.zeros((len(ids), K), np.uint8)
+    sa = np.ones((len(ids), K // 128), np.float32)
+    real = tok >= 0
+    a[real], sa[real] = xa[tok[real]], sa_tok.T[tok[real]]
+    b = np.empty((G, N, K), np.uint8)
+    sb = np.empty((G, N // 128, K // 128), np.float32)
+    for g in range(G):
+        b[g], sb[g] = gen.make_rhs(N, K, 43 + g, fb)
+    d = sentinel_bf16((len(ids), N))
+    ops.dg_fp8_grouped_gemm_contiguous_fmt(dev(a), dev(sa), dev(b), dev(sb), dev(ids), fa, fb, d=d)
+    torch.cuda.synchronize()
+    got = bits(d)
+    assert np.all(got[~real] == SENTINEL)
+    for g in range(G):
+        rows = np.nonzero(ids == g)[0]
+        if len(rows):
+            ref = oracle.gemm_nt_fmt(a[rows], fa, sa[rows], b[g], fb, sb[g])
+            assert_close(got[rows], ref, "%s x %s expert %d" % (fa, fb, g))
+
+
+@pytest.mark.parametrize("fa,fb", FMT_CASES)
+def test_masked_fmt_matches_per_group_dense_oracle(gpu_device, fa, fb):
+    G, M_max, N, K = 4, 200, 512, 640
+    mm = np.array([0, 200, 73, 129], np.int32)
+    a = np.empty((G, M_max, K), np.uint8)
+    sa = np.empty((G, M_max, K // 128), np.float32)
+    b = np.empty((G, N, K), np.uint8)
+    sb = np.empty((G, N // 128, K // 128), np.float32)
+    for g in range(G):
+        a[g], sat = gen.make_lhs(M_max, K, 52 + g, fa)
+        sa[g] = sat.T
+        b[g], sb[g] = gen.make_rhs(N, K, 62 + g, fb)
+    d = sentinel_bf16((G, M_max, N))
+    ops.dg_fp8_grouped_gemm_masked_fmt(dev(a), dev(sa), dev(b), dev(sb), dev(mm), fa, fb, d=d)
+    torch.cuda.synchronize()
+    got = bits(d)
+    for g in range(G):
+        c = int(mm[g])
+        assert np.all(got[g, c:] == SENTINEL)
+        if c:
+            ref = oracle.gemm_nt_fmt(a[g, :c], fa, sa[g, :c], b[g], fb, sb[g])
+            assert_close(got[g, :c], ref, "%s x %s group %d" % (fa, fb, g))
