@@ -107,7 +107,12 @@ class Launcher:
             d = torch.empty((p.M_total, p.N), dtype=torch.bfloat16, device=dev)
             for i in range(n):
                 self.copies.append(base if i == 0 else tuple(x.clone() for x in base))
-            self.fn = lambda c: ops.dg_fp8_grouped_gemm_contiguous(c[0], c[1].t(), c[2], c[3], c[4], d=d)
+            if gen.CONFIGS[name].get("segments"):
+                layout = t(gen.segment_layout(p.counts))
+                self.fn = lambda c: ops.dg_fp8_grouped_gemm_contiguous_layout(c[0], c[1].t(), c[2], c[3], c[4],
+                                                                              layout, d=d)
+            else:
+                self.fn = lambda c: ops.dg_fp8_grouped_gemm_contiguous(c[0], c[1].t(), c[2], c[3], c[4], d=d)
         else:
             one = p.a.nbytes + p.b.nbytes
             n = max(1, min(8, -(-ROTATE_BYTES // one))) if rotate else 1
@@ -226,7 +231,8 @@ def time_moe_layer(steps, warmup):
     """The contiguous MoE step end to end on the contiguous workload's shape
     (8 experts, 8192 tokens, K 7168, N 4096, top-1 routing seed): routing ->
     bf16 activations quantised into the padded layout -> grouped GEMM over
-    the layout's capacity, written straight to token order. Whole step timed
+    the layout's capacity on tiles that follow the experts' segments, written
+    straight to token order. Whole step timed
     as one graph of `steps` repetitions; also the step with a separate
     un-permute, and each stage on its own."""
     import torch
@@ -269,7 +275,7 @@ def time_moe_layer(steps, warmup):
         ops.dg_moe_unpermute(d, row, out=out)
 
     def gemm_to_tokens(i):
-        ops.dg_fp8_grouped_gemm_contiguous_to_tokens(q, s, bs[i % n], sbd, ids, tok, T, out=out)
+        ops.dg_fp8_grouped_gemm_contiguous_to_tokens(q, s, bs[i % n], sbd, ids, tok, T, layout=layout, out=out)
 
     def step(i):  # the un-permute folded into the GEMM's epilogue
         route(i), quant(i), gemm_to_tokens(i)

@@ -22,8 +22,11 @@ SIGNATURES = {
                                                       _p, _i64, _i64, _i64, _p, _p, _i64,
                                                       _i64, _i64, _i64, _i64, _p]),
     "dg_fp8_grouped_gemm_contiguous_to_tokens": (ctypes.c_int, [_p, _i64, _p, _i64, _i64, _p, _i64, _i64,
-                                                                _p, _i64, _i64, _i64, _p, _p, _p, _i64, _i64,
+                                                                _p, _i64, _i64, _i64, _p, _p, _p, _p, _i64, _i64,
                                                                 _i64, _i64, _i64, _i64, _p]),
+    "dg_fp8_grouped_gemm_contiguous_layout": (ctypes.c_int, [_p, _i64, _p, _i64, _i64, _p, _i64, _i64,
+                                                             _p, _i64, _i64, _i64, _p, _p, _p, _i64,
+                                                             _i64, _i64, _i64, _i64, _p]),
     "dg_fp8_grouped_gemm_contiguous_fmt": (ctypes.c_int, [_p, ctypes.c_int, _i64, _p, _i64, _i64, _p, ctypes.c_int,
                                                           _i64, _i64, _p, _i64, _i64, _i64, _p, _p, _i64,
                                                           _i64, _i64, _i64, _i64, _p]),

@@ -185,6 +185,27 @@ int launch_tiles(dgk::Params &p, int groups, int cus, hipStream_t stream)
     return e == hipSuccess ? DG_OK : fail_hip(e);
 }
 
+// Contiguous layout on segment-aligned tiles (tile_kernel's SEG mode). The
+// real tile count depends on the device-side layout; the grid covers the
+// bound (ceil(M_total / 256) + G) x tiles_n and the kernel skips the rest.
+template <class C, bool SCATTER>
+int launch_contiguous_seg(dgk::Params &p, int cus, hipStream_t stream)
+{
+    if (p.N % C::kBN != 0)
+        return DG_ERR_UNSUPPORTED;
+    p.tiles_n = p.N / C::kBN;
+    p.tiles_m = (p.M + 255) / 256 + p.G;
+    const int64_t tiles = (int64_t)p.tiles_m * p.tiles_n;
+    if (tiles > kInt32Max)
+        return DG_ERR_UNSUPPORTED;
+    p.num_tiles = (int)tiles;
+    const int grid = p.num_tiles < cus ? p.num_tiles : cus;
+    hipLaunchKernelGGL((dgk::tile_kernel<dgk::kContiguous, C, 0, SCATTER, true>), dim3(grid), dim3(C::kThreads), 0,
+                       stream, p);
+    hipError_t e = hipGetLastError();
+    return e == hipSuccess ? DG_OK : fail_hip(e);
+}
+
 // launch_tiles with the operand formats chosen at run time (bit 0: A is e5m2,
 // bit 1: B is e5m2); the formats only set the MFMA's format selectors.
 template <int L, class C>
@@ -523,7 +544,7 @@ int contiguous_impl(const void *A, int64_t lda, const float *sA, int64_t sa_stri
                     const void *B, int64_t ldb, int64_t b_stride_g, const float *sB, int64_t sb_stride_g,
                     int64_t sb_stride_nb, int64_t sb_stride_kb, const int32_t *expert_ids,
                     const int32_t *token_of_row, void *D, int64_t ldd, int64_t d_rows, int64_t M_total, int64_t N,
-                    int64_t K, int64_t G, void *stream, int fmt = 0)
+                    int64_t K, int64_t G, void *stream, int fmt = 0, const int32_t *layout = nullptr)
 {
     int st = check_common_shape(M_total, N, K);
     if (st != DG_OK)
@@ -540,8 +561,10 @@ int contiguous_impl(const void *A, int64_t lda, const float *sA, int64_t sa_stri
         return DG_OK;
     if (!A || !sA || !B || !sB || !expert_ids || !D)
         return DG_ERR_NULL_POINTER;
-    if (token_of_row && !aligned(token_of_row, 4))
+    if ((token_of_row && !aligned(token_of_row, 4)) || (layout && !aligned(layout, 4)))
         return DG_ERR_MISALIGNED;
+    if (layout && G > dgm::kMaxExperts)
+        return DG_ERR_UNSUPPORTED;
     if (lda < K || ldb < K || ldd < N || sa_stride_m < 0 || sa_stride_kb < 0 || sb_stride_nb < 0 ||
         sb_stride_kb < 0 || sb_stride_g < 0 || (G > 1 && b_stride_g < (N - 1) * ldb + K))
         return DG_ERR_BAD_STRIDE;
@@ -550,7 +573,8 @@ int contiguous_impl(const void *A, int64_t lda, const float *sA, int64_t sa_stri
         return DG_ERR_MISALIGNED;
     const int64_t nkb = K / 128;
     const Extent ed = extent(D, 2, (d_rows - 1) * ldd + N - 1);
-    if (token_of_row && overlaps(ed, extent(token_of_row, 4, M_total - 1)))
+    if ((token_of_row && overlaps(ed, extent(token_of_row, 4, M_total - 1))) ||
+        (layout && overlaps(ed, extent(layout, 4, G))))
         return DG_ERR_ALIASING;
     if (overlaps(ed, extent(A, 1, (M_total - 1) * lda + K - 1)) ||
         overlaps(ed, extent(B, 1, (G - 1) * b_stride_g + (N - 1) * ldb + K - 1)) ||
@@ -570,9 +594,18 @@ int contiguous_impl(const void *A, int64_t lda, const float *sA, int64_t sa_stri
     p.D = (uint16_t *)D; p.ldd = ldd;
     p.ids = expert_ids;
     p.row_dst = token_of_row; p.dst_rows = (int)d_rows;
+    p.layout = layout;
     p.M = (int)M_total; p.N = (int)N; p.K = (int)K; p.G = (int)G;
     if (!offsets_fit(lda, ldb, sa_stride_m))
         return DG_ERR_UNSUPPORTED;
+    if (layout) {
+        const bool wide = N % 256 == 0;
+        if (token_of_row)
+            return wide ? launch_contiguous_seg<CfgBig, true>(p, dev.cus, (hipStream_t)stream)
+                        : launch_contiguous_seg<CfgDense, true>(p, dev.cus, (hipStream_t)stream);
+        return wide ? launch_contiguous_seg<CfgBig, false>(p, dev.cus, (hipStream_t)stream)
+                    : launch_contiguous_seg<CfgDense, false>(p, dev.cus, (hipStream_t)stream);
+    }
     if (token_of_row) {
         if (N % 256 == 0)
             return launch_tiles<dgk::kContiguous, CfgBig, 0, true>(p, 1, dev.cus, (hipStream_t)stream);
@@ -736,14 +769,29 @@ int dg_fp8_grouped_gemm_contiguous_to_tokens(const void *A, int64_t lda, const f
                                              int64_t sa_stride_kb, const void *B, int64_t ldb, int64_t b_stride_g,
                                              const float *sB, int64_t sb_stride_g, int64_t sb_stride_nb,
                                              int64_t sb_stride_kb, const int32_t *expert_ids,
-                                             const int32_t *token_of_row, void *out, int64_t ldo, int64_t T,
-                                             int64_t M_total, int64_t N, int64_t K, int64_t G, void *stream)
+                                             const int32_t *token_of_row, const int32_t *layout, void *out,
+                                             int64_t ldo, int64_t T, int64_t M_total, int64_t N, int64_t K,
+                                             int64_t G, void *stream)
 {
     if (M_total > 0 && N > 0 && G > 0 && T > 0 && !token_of_row)
         return DG_ERR_NULL_POINTER;
     return contiguous_impl(A, lda, sA, sa_stride_m, sa_stride_kb, B, ldb, b_stride_g, sB, sb_stride_g,
                            sb_stride_nb, sb_stride_kb, expert_ids, token_of_row, out, ldo, T, M_total, N, K, G,
-                           stream);
+                           stream, 0, layout);
+}
+
+int dg_fp8_grouped_gemm_contiguous_layout(const void *A, int64_t lda, const float *sA, int64_t sa_stride_m,
+                                          int64_t sa_stride_kb, const void *B, int64_t ldb, int64_t b_stride_g,
+                                          const float *sB, int64_t sb_stride_g, int64_t sb_stride_nb,
+                                          int64_t sb_stride_kb, const int32_t *expert_ids, const int32_t *layout,
+                                          void *D, int64_t ldd, int64_t M_total, int64_t N, int64_t K, int64_t G,
+                                          void *stream)
+{
+    if (M_total > 0 && N > 0 && G > 0 && !layout)
+        return DG_ERR_NULL_POINTER;
+    return contiguous_impl(A, lda, sA, sa_stride_m, sa_stride_kb, B, ldb, b_stride_g, sB, sb_stride_g,
+                           sb_stride_nb, sb_stride_kb, expert_ids, nullptr, D, ldd, M_total, M_total, N, K, G,
+                           stream, 0, layout);
 }
 
 int dg_fp8_grouped_gemm_masked(const void *A, int64_t lda, int64_t a_stride_g, const float *sA, int64_t sa_stride_g,

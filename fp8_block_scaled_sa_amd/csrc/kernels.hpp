@@ -62,6 +62,9 @@ struct Params {
     // result goes to row row_dst[m] of D, for 0 <= row_dst[m] < dst_rows.
     const int32_t *row_dst;
     int dst_rows;
+    // Contiguous layout with segment offsets: layout[e] is the first row of
+    // expert e's segment (a multiple of 128 rows), layout[G] the rows used.
+    const int32_t *layout;
 };
 
 // One e4m3 x e4m3 -> fp32 MFMA over a 16x16x128 block, C = 0 + A.B.
@@ -300,7 +303,7 @@ __device__ __forceinline__ void wait_stage(int per_stage)
         wait_vmcnt<(SEGW + 2) * LATER>();
 }
 
-template <int L, class C, int F = 0, bool SCATTER = false>
+template <int L, class C, int F = 0, bool SCATTER = false, bool SEG = false>
 __global__ void __launch_bounds__(C::kThreads, 1) tile_kernel(Params p)
 {
     constexpr int BM = C::kBM, BN = C::kBN, S = C::kStages;
@@ -309,6 +312,7 @@ __global__ void __launch_bounds__(C::kThreads, 1) tile_kernel(Params p)
     static_assert(L != kContiguous || BM <= 256, "contiguous tiles span at most two 128-row blocks");
     static_assert(L != kContiguous || C::kWM <= 128, "a wave's rows lie in one 128-row block");
     static_assert(L != kContiguous || BM == 256 || 128 % BM == 0, "contiguous tile rows");
+    static_assert(!SEG || (L == kContiguous && BM == 256), "segment tiles are 256 or 128 rows of one expert");
 
     __shared__ __attribute__((aligned(1024))) uint8_t smem[C::kSmemBytes];
 
@@ -326,19 +330,69 @@ __global__ void __launch_bounds__(C::kThreads, 1) tile_kernel(Params p)
     const bool loads_sb = wave == C::kWaves - 1;
     const int per_stage = SEGW + (loads_sa ? 1 : 0) + (loads_sb ? 1 : 0);  // DMA ops per stage
 
+    // SEG: tiles follow the experts' segments, so that every tile holds rows
+    // of one expert only: first the whole 256-row tiles of every segment
+    // (expert by expert), then each segment's last 128 rows where its size is
+    // an odd multiple of 128. full / half: how many of each.
+    int seg_full = 0, seg_half = 0;
+    if constexpr (SEG) {
+        for (int e = 0; e < p.G; ++e) {
+            const int sz = p.layout[e + 1] - p.layout[e];
+            if (sz > 0) {
+                seg_full += sz >> 8;
+                seg_half += (sz >> 7) & 1;
+            }
+        }
+    }
+
     for (int t = xcd_local_id(blockIdx.x, gridDim.x); t < p.num_tiles; t += gridDim.x) {
         int g = 0, mt, nt;
         // split-K: work item t is K slice t % ks of tile t / ks
         const int slice = t % ks;
         const int kb_lo = (int)((int64_t)slice * nk_all / ks);
         const int nk = (int)((int64_t)(slice + 1) * nk_all / ks) - kb_lo;  // K blocks of this item
-        if (L == kMasked) {
+        int seg_m0 = 0, seg_rows = 0, seg_e = 0;
+        if constexpr (SEG) {
+            mt = 0;
+            if (t < seg_full * p.tiles_n) {
+                int ft;
+                tile_coords(t, seg_full, p.tiles_n, C::kGroupM, ft, nt);
+                int before = 0;  // whole tiles of the experts before seg_e
+                for (seg_e = 0; seg_e < p.G; ++seg_e) {
+                    const int sz = p.layout[seg_e + 1] - p.layout[seg_e];
+                    const int f = sz > 0 ? sz >> 8 : 0;
+                    if (ft < before + f)
+                        break;
+                    before += f;
+                }
+                seg_m0 = p.layout[seg_e] + 256 * (ft - before);
+                seg_rows = 256;
+            } else {
+                const int h = (t - seg_full * p.tiles_n) / p.tiles_n;
+                if (h >= seg_half)
+                    continue;  // past the real tiles (uniform over the workgroup)
+                nt = t - seg_full * p.tiles_n - h * p.tiles_n;
+                int seen = 0;
+                for (seg_e = 0; seg_e < p.G; ++seg_e) {
+                    const int sz = p.layout[seg_e + 1] - p.layout[seg_e];
+                    if (sz > 0 && ((sz >> 7) & 1)) {
+                        if (seen == h)
+                            break;
+                        ++seen;
+                    }
+                }
+                seg_m0 = p.layout[seg_e] + ((p.layout[seg_e + 1] - p.layout[seg_e]) & ~255);
+                seg_rows = 128;
+            }
+            if (seg_m0 < 0 || seg_m0 >= p.M)
+                continue;  // a layout that does not fit the rows: nothing to do
+        } else if (L == kMasked) {
             g = t / tiles_per_group;
             tile_coords(t - g * tiles_per_group, p.tiles_m, p.tiles_n, C::kGroupM, mt, nt);
         } else {
             tile_coords(t / ks, p.tiles_m, p.tiles_n, C::kGroupM, mt, nt);
         }
-        const int m0 = mt * BM, n0 = nt * BN;
+        const int m0 = SEG ? seg_m0 : mt * BM, n0 = nt * BN;
 
         int rows;        // valid rows of this tile (the rest re-read the last valid row)
         int limit = 0;   // masked: valid rows of the group
@@ -351,6 +405,9 @@ __global__ void __launch_bounds__(C::kThreads, 1) tile_kernel(Params p)
             if (m0 >= limit)
                 continue;  // uniform over the workgroup
             rows = min(BM, limit - m0);
+        } else if (SEG) {
+            ex0 = ex1 = seg_e;
+            rows = min(seg_rows, p.M - m0);
         } else {
             // Expert of an aligned 128-row block: the largest valid id in it
             // (-1 if it holds padding only or lies past M_total).

@@ -135,15 +135,20 @@ def dg_fp8_grouped_gemm_contiguous(a, sa, b, sb, expert_ids, d=None, stream=None
     return d
 
 
-def dg_fp8_grouped_gemm_contiguous_to_tokens(a, sa, b, sb, expert_ids, token_of_row, T, out=None, stream=None):
+def dg_fp8_grouped_gemm_contiguous_to_tokens(a, sa, b, sb, expert_ids, token_of_row, T, layout=None, out=None,
+                                             stream=None):
     """The contiguous grouped GEMM with row r of the result written to
-    out[token_of_row[r]] (out [T, N] bf16; rows of dropped tokens untouched)."""
+    out[token_of_row[r]] (out [T, N] bf16; rows of dropped tokens untouched).
+    With the routing's segment offsets `layout` [G+1] the tiles follow the
+    experts' segments."""
     _codes(a, "a", 2), _codes(b, "b", 3), _scales(sa, "sa", 2), _scales(sb, "sb", 3)
     M_total, K = a.shape
     G, N, _ = b.shape
     for t, name in ((expert_ids, "expert_ids"), (token_of_row, "token_of_row")):
         if t.dtype != torch.int32 or tuple(t.shape) != (M_total,):
             raise ValueError("%s must be int32 [M_total]" % name)
+    if layout is not None and (layout.dtype != torch.int32 or tuple(layout.shape) != (G + 1,)):
+        raise ValueError("layout must be int32 [G+1]")
     if out is None:
         out = torch.empty((T, N), dtype=torch.bfloat16, device=a.device)
     if out.dtype != torch.bfloat16 or tuple(out.shape) != (T, N) or out.stride(-1) != 1:
@@ -152,10 +157,31 @@ def dg_fp8_grouped_gemm_contiguous_to_tokens(a, sa, b, sb, expert_ids, token_of_
     st = lib.dg_fp8_grouped_gemm_contiguous_to_tokens(
         _dev(a, "a"), a.stride(0), _dev(sa, "sa"), sa.stride(0), sa.stride(1),
         _dev(b, "b"), b.stride(1), b.stride(0), _dev(sb, "sb"), sb.stride(0), sb.stride(1), sb.stride(2),
-        _dev(expert_ids, "expert_ids"), _dev(token_of_row, "token_of_row"), _dev(out, "out"), out.stride(0), T,
+        _dev(expert_ids, "expert_ids"), _dev(token_of_row, "token_of_row"),
+        None if layout is None else _dev(layout, "layout"), _dev(out, "out"), out.stride(0), T,
         M_total, N, K, G, _stream(stream))
     _check(st, "dg_fp8_grouped_gemm_contiguous_to_tokens")
     return out
+
+
+def dg_fp8_grouped_gemm_contiguous_layout(a, sa, b, sb, expert_ids, layout, d=None, stream=None):
+    """The contiguous grouped GEMM with the experts' segment offsets
+    (layout [G+1] int32): tiles follow the segments."""
+    _codes(a, "a", 2), _codes(b, "b", 3), _scales(sa, "sa", 2), _scales(sb, "sb", 3)
+    M_total, K = a.shape
+    G, N, _ = b.shape
+    if layout.dtype != torch.int32 or tuple(layout.shape) != (G + 1,):
+        raise ValueError("layout must be int32 [G+1]")
+    if d is None:
+        d = torch.empty((M_total, N), dtype=torch.bfloat16, device=a.device)
+    lib = _lib.load()
+    st = lib.dg_fp8_grouped_gemm_contiguous_layout(
+        _dev(a, "a"), a.stride(0), _dev(sa, "sa"), sa.stride(0), sa.stride(1),
+        _dev(b, "b"), b.stride(1), b.stride(0), _dev(sb, "sb"), sb.stride(0), sb.stride(1), sb.stride(2),
+        _dev(expert_ids, "expert_ids"), _dev(layout, "layout"), _dev(d, "d"), d.stride(0),
+        M_total, N, K, G, _stream(stream))
+    _check(st, "dg_fp8_grouped_gemm_contiguous_layout")
+    return d
 
 
 def dg_fp8_grouped_gemm_masked(a, sa, b, sb, masked_m, d=None, stream=None):

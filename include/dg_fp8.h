@@ -168,11 +168,35 @@ int dg_fp8_grouped_gemm_contiguous(const void *A, int64_t lda,
                                    int64_t M_total, int64_t N, int64_t K, int64_t G, void *stream);
 
 /*
+ * The contiguous grouped GEMM given each expert's segment offsets as well
+ * (the token offsets of the routing: rkmt.cn walkthrough, §5.3):
+ *   layout [G + 1] int32 (device): layout[e] is the first row of expert e's
+ *   segment, layout[G] the rows used, as written by dg_moe_route_contiguous.
+ * Every segment must be a multiple of 128 rows and hold only rows of its
+ * expert (or padding rows with id -1), as the contiguous layout requires.
+ * With the offsets the GEMM tiles each segment on its own: whole 256-row
+ * tiles first, then the segments' last 128 rows, so no tile spans two
+ * experts. Result and other arguments as dg_fp8_grouped_gemm_contiguous;
+ * 1 <= G <= 1024. A layout that does not match expert_ids leaves rows
+ * unwritten (no fault).
+ */
+int dg_fp8_grouped_gemm_contiguous_layout(const void *A, int64_t lda,
+                                          const float *sA, int64_t sa_stride_m, int64_t sa_stride_kb,
+                                          const void *B, int64_t ldb, int64_t b_stride_g,
+                                          const float *sB, int64_t sb_stride_g, int64_t sb_stride_nb,
+                                          int64_t sb_stride_kb,
+                                          const int32_t *expert_ids, const int32_t *layout,
+                                          void *D, int64_t ldd,
+                                          int64_t M_total, int64_t N, int64_t K, int64_t G, void *stream);
+
+/*
  * The contiguous grouped GEMM written straight to token order: row r of the
  * result (a row dg_fp8_grouped_gemm_contiguous would write) goes to row
  * token_of_row[r] of out instead of row r of D, when 0 <= token_of_row[r] < T.
  * This folds dg_moe_unpermute into the GEMM's epilogue.
  *   token_of_row [M_total] int32 (device), as written by dg_moe_route_contiguous
+ *   layout [G + 1] int32 (device) or NULL: segment offsets as in
+ *   dg_fp8_grouped_gemm_contiguous_layout (then tiles follow the segments)
  *   out [T, N] bf16, row stride ldo: rows of tokens that no row names (dropped
  *   tokens) are NOT written.
  * Precondition: no token appears twice in token_of_row (the routing call
@@ -186,6 +210,7 @@ int dg_fp8_grouped_gemm_contiguous_to_tokens(const void *A, int64_t lda,
                                              const float *sB, int64_t sb_stride_g, int64_t sb_stride_nb,
                                              int64_t sb_stride_kb,
                                              const int32_t *expert_ids, const int32_t *token_of_row,
+                                             const int32_t *layout,
                                              void *out, int64_t ldo, int64_t T,
                                              int64_t M_total, int64_t N, int64_t K, int64_t G, void *stream);
 

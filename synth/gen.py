@@ -235,6 +235,9 @@ CONFIGS = {
     "prefill_8192x7168x2048": dict(kind="dense", M=8192, N=7168, K=2048, seeds=(311, 312)),
     "moe_contiguous_g8_t8192": dict(kind="contiguous", G=8, tokens=8192, N=4096, K=7168,
                                     seeds=(401, 402, 403)),
+    # the same problem with the experts' segment offsets passed to the GEMM
+    "moe_contiguous_g8_t8192_seg": dict(kind="contiguous", G=8, tokens=8192, N=4096, K=7168,
+                                        seeds=(401, 402, 403), segments=True),
     "moe_masked_g32_m256": dict(kind="masked", G=32, M_max=256, N=4096, K=7168,
                                 seeds=(501, 502, 504)),
 }
@@ -252,6 +255,12 @@ def make_activations(name: str) -> np.ndarray:
     """fp32 activations of a quantiser workload (bf16 workloads round them)."""
     c = QUANT_CONFIGS[name]
     return normal_with_outliers(np.random.Generator(np.random.PCG64(c["seed"])), (c["M"], c["K"]))
+
+
+def segment_layout(counts: np.ndarray) -> np.ndarray:
+    """First row of each expert's segment (segments padded to 128), then the rows used."""
+    padded = (np.asarray(counts, np.int64) + BLOCK - 1) // BLOCK * BLOCK
+    return np.concatenate([[0], np.cumsum(padded)]).astype(np.int32)
 
 
 def make_config(name: str):

@@ -295,7 +295,7 @@ def test_fmt_empty():
 
 def contig_tokens(**kw):
     args = dict(A=A, lda=512, sA=SA, sa_m=1, sa_kb=256, B=B, ldb=512, b_stride_g=256 * 512,
-                sB=SB, sb_g=8, sb_nb=4, sb_kb=1, ids=IDS, tok=E, out=D, ldo=256, T=200,
+                sB=SB, sb_g=8, sb_nb=4, sb_kb=1, ids=IDS, tok=E, layout=None, out=D, ldo=256, T=200,
                 M_total=256, N=256, K=512, G=4, stream=None)
     args.update(kw)
     return _lib.load().dg_fp8_grouped_gemm_contiguous_to_tokens(*args.values())
@@ -349,3 +349,26 @@ def test_grouped_fmt_validation(fn, kw, status):
 
 def test_grouped_fmt_empty():
     assert contig_fmt(M_total=0) == DG_OK and masked_fmt(G=0) == DG_OK
+
+
+def contig_layout(**kw):
+    args = dict(A=A, lda=512, sA=SA, sa_m=1, sa_kb=256, B=B, ldb=512, b_stride_g=256 * 512,
+                sB=SB, sb_g=8, sb_nb=4, sb_kb=1, ids=IDS, layout=LAY, D=D, ldd=256,
+                M_total=256, N=256, K=512, G=4, stream=None)
+    args.update(kw)
+    return _lib.load().dg_fp8_grouped_gemm_contiguous_layout(*args.values())
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(layout=None), DG_ERR_NULL_POINTER),
+    (dict(layout=LAY + 2), DG_ERR_MISALIGNED),
+    (dict(G=1025), DG_ERR_UNSUPPORTED),
+    (dict(D=LAY - 64), DG_ERR_ALIASING),
+    (dict(M_total=200), DG_ERR_BAD_SHAPE),
+])
+def test_contiguous_layout_validation(kw, status):
+    assert contig_layout(**kw) == status
+
+
+def test_contiguous_layout_empty():
+    assert contig_layout(M_total=0, layout=None) == DG_OK

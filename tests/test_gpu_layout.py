@@ -1,0 +1,100 @@
+"""Contiguous grouped GEMM tiled along the experts' segments (layout given).
+
+The per-element arithmetic does not depend on how the rows are tiled, so the
+segment-tiled result must equal the uniform-grid result bit for bit; it is
+also held against the oracle, padding rows must stay untouched, and a layout
+that does not fit the rows must write nothing (and not fault).
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from fp8_block_scaled_sa_amd import ops
+from synth import gen
+from tests.check import SENTINEL, assert_close
+from tests.gpu_util import bits, dev, sentinel_bf16
+
+pytestmark = pytest.mark.gpu
+
+
+def layout_of(counts):
+    padded = (np.asarray(counts) + 127) // 128 * 128
+    return np.concatenate([[0], np.cumsum(padded)]).astype(np.int32)
+
+
+def run_both(c, layout):
+    args = (dev(c.a), dev(c.sa_t).t(), dev(c.b), dev(c.sb), dev(c.ids))
+    d_grid = sentinel_bf16((c.M_total, c.N))
+    ops.dg_fp8_grouped_gemm_contiguous(*args, d=d_grid)
+    d_seg = sentinel_bf16((c.M_total, c.N))
+    ops.dg_fp8_grouped_gemm_contiguous_layout(*args, dev(layout), d=d_seg)
+    torch.cuda.synchronize()
+    return bits(d_grid), bits(d_seg)
+
+
+@pytest.mark.parametrize("G,T,N,K,seed", [
+    (4, 700, 256, 512, 1),      # 256x256 tiles
+    (5, 900, 384, 640, 2),      # 256x128 tiles
+    (8, 1500, 512, 256, 3),
+    (3, 130, 256, 128, 4),      # one 256-row tile and a 128-row tail
+    (6, 400, 256, 384, 5),      # empty experts
+])
+def test_segment_tiles_equal_grid_tiles_and_oracle(gpu_device, G, T, N, K, seed):
+    rng = np.random.default_rng(seed)
+    p = rng.dirichlet(np.ones(G) * 0.7)
+    if seed == 5:
+        p[1] = p[4] = 0
+        p /= p.sum()
+    e = rng.choice(G, T, p=p).astype(np.int32)
+    c = gen.make_contiguous(G, T, N, K, 700 + seed, 800 + seed, 0, expert_of_token=e)
+    layout = layout_of(c.counts)
+    assert layout[-1] == c.M_total
+    grid, seg = run_both(c, layout)
+    assert np.array_equal(seg, grid)
+    valid = c.ids >= 0
+    assert np.all(seg[~valid] == SENTINEL)
+    ref = oracle.grouped_contiguous(c.a, c.sa_t.T, c.b, c.sb, c.ids, np.full((c.M_total, N), SENTINEL, np.uint16))
+    assert_close(seg[valid], ref[valid], "segment tiles G=%d T=%d" % (G, T))
+
+
+def test_segment_tiles_full_size(gpu_device):
+    """The contiguous MoE workload (8 experts, 8192 tokens, N 4096, K 7168):
+    segment tiles give exactly the uniform-grid result."""
+    c = gen.make_config("moe_contiguous_g8_t8192")
+    grid, seg = run_both(c, layout_of(c.counts))
+    assert np.array_equal(seg, grid)
+    assert not np.any(grid[c.ids >= 0] == SENTINEL)
+
+
+def test_to_tokens_with_layout(gpu_device):
+    T, G, N, K = 700, 5, 384, 1024
+    x = torch.from_numpy(gen.normal_with_outliers(np.random.Generator(np.random.PCG64(941)), (T, K)))
+    e = np.random.Generator(np.random.PCG64(942)).choice(G, T).astype(np.int32)
+    e[::13] = -1
+    b, sb = gen.make_grouped_rhs(G, N, K, 943)
+    bd, sbd = dev(b), dev(sb)
+    row, ids, tok, layout = ops.dg_moe_route_contiguous(dev(e), G)
+    q, s = ops.dg_fp8_quantize_1x128_gather(x.cuda(), tok)
+    out0 = sentinel_bf16((T, N))
+    ops.dg_fp8_grouped_gemm_contiguous_to_tokens(q, s, bd, sbd, ids, tok, T, out=out0)
+    out1 = sentinel_bf16((T, N))
+    ops.dg_fp8_grouped_gemm_contiguous_to_tokens(q, s, bd, sbd, ids, tok, T, layout=layout, out=out1)
+    torch.cuda.synchronize()
+    assert np.array_equal(bits(out0), bits(out1))
+    assert np.all(bits(out1)[e < 0] == SENTINEL)
+
+
+@pytest.mark.parametrize("kind", ["zeros", "past_the_rows", "negative"])
+def test_layout_that_does_not_fit_writes_nothing(gpu_device, kind):
+    G, T, N, K = 4, 300, 256, 256
+    e = np.random.default_rng(6).choice(G, T).astype(np.int32)
+    c = gen.make_contiguous(G, T, N, K, 951, 952, 0, expert_of_token=e)
+    if kind == "zeros":
+        layout = np.zeros(G + 1, np.int32)
+    elif kind == "past_the_rows":
+        layout = (c.M_total + 128 * np.arange(G + 1)).astype(np.int32)
+    else:
+        layout = (-4096 + 256 * np.arange(G + 1)).astype(np.int32)
+    _, seg = run_both(c, layout)
+    assert np.all(seg == SENTINEL)
