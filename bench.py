@@ -284,12 +284,13 @@ def time_moe_layer(steps, warmup):
         route(i), quant(i), gemm(i), unperm(i)
 
     def graph_us(fn):
-        for i in range(warmup):
-            fn(i)
-        torch.cuda.synchronize()
         graph = torch.cuda.CUDAGraph()
         cap = torch.cuda.Stream()
         cap.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(cap):    # warm-up on the capture stream also sets up its split-K workspace
+            for i in range(warmup):
+                fn(i)
+        torch.cuda.synchronize()
         with torch.cuda.graph(graph, stream=cap):
             for i in range(steps):
                 fn(i)

@@ -148,6 +148,7 @@ using CfgBig = dgk::TileCfg<256, 256, 2, 4, 2, 4>;  // 2 stages of 66 KB; N % 25
 using CfgBigStreamB = dgk::TileCfg<256, 256, 2, 4, 2, 4, true>;
 using CfgWide = dgk::TileCfg<128, 256, 2, 2, 3, 8>;
 using CfgNarrow = dgk::TileCfg<128, 128, 2, 2, 4, 8>;
+using CfgWide8 = dgk::TileCfg<128, 256, 2, 4, 2, 4>;  // segment tails next to CfgBig (8 waves, 8% faster than 4 there)
 
 // Optional override of the kernel choice, read once: DG_TILE=<index>, for
 // measurements. 1, 2, 4: dense on 256x128 (4 waves), 128x128 or 256x128 tiles
@@ -156,6 +157,7 @@ using CfgNarrow = dgk::TileCfg<128, 128, 2, 2, 4, 8>;
 // decode kernels up to M = 16 / all older decode kernels up to 64; 15:
 // split-K always on 256-wide tiles;
 // 16: no split-K; 18: no cut of a partly filled last round of 256x256 tiles;
+// 23: segment tails not split over K;
 // 2, 3, 4 also pick the contiguous layout's tile shape.
 int tile_override()
 {
@@ -186,11 +188,15 @@ int launch_tiles(dgk::Params &p, int groups, int cus, hipStream_t stream)
 }
 
 // Contiguous layout on segment-aligned tiles (tile_kernel's SEG mode). The
-// real tile count depends on the device-side layout; the grid covers the
-// bound (ceil(M_total / 256) + G) x tiles_n and the kernel skips the rest.
-template <class C, bool SCATTER>
+// real tile count depends on the device-side layout; each grid covers a bound
+// and the kernel skips the rest. With a workspace, the whole 256-row tiles run
+// first (they fill whole rounds when the segments are long), then the 128-row
+// tails split over K (their rows are few, but each would otherwise take about
+// as long as a whole tile), then a reduction adds the tails' slices in order.
+template <class C, class CT, bool SCATTER>
 int launch_contiguous_seg(dgk::Params &p, int cus, hipStream_t stream)
 {
+    static_assert(C::kBM == 256 && CT::kBM == 128, "whole tiles 256 rows, tails 128");
     if (p.N % C::kBN != 0)
         return DG_ERR_UNSUPPORTED;
     p.tiles_n = p.N / C::kBN;
@@ -199,10 +205,40 @@ int launch_contiguous_seg(dgk::Params &p, int cus, hipStream_t stream)
     if (tiles > kInt32Max)
         return DG_ERR_UNSUPPORTED;
     p.num_tiles = (int)tiles;
-    const int grid = p.num_tiles < cus ? p.num_tiles : cus;
-    hipLaunchKernelGGL((dgk::tile_kernel<dgk::kContiguous, C, 0, SCATTER, true>), dim3(grid), dim3(C::kThreads), 0,
-                       stream, p);
+    p.seg_mode = 0;
+    p.ksplit = 1;
+    // At most this many K slices per tail, at least four K blocks each; the
+    // kernels pick the count from the number of tails they find. No split
+    // when the tails alone would fill two rounds of the CUs.
+    if (p.N % CT::kBN != 0)
+        return DG_ERR_UNSUPPORTED;
+    const int64_t tail_tiles = (int64_t)p.G * (p.N / CT::kBN);
+    const int ks = tail_tiles >= 2 * (int64_t)cus || tile_override() == 23 ? 1 : std::min(dgk::kMaxTailSplit, (p.K / 128) / 4);
+    const size_t ws_bytes = (size_t)ks * p.G * 128 * p.N * sizeof(float);
+    float *ws = (ks >= 2 && ws_bytes <= ((size_t)1 << 30)) ? stream_workspace(stream, ws_bytes) : nullptr;
+    if (ws)
+        p.seg_mode = 1;
+    hipLaunchKernelGGL((dgk::tile_kernel<dgk::kContiguous, C, 0, SCATTER, true>),
+                       dim3(p.num_tiles < cus ? p.num_tiles : cus), dim3(C::kThreads), 0, stream, p);
     hipError_t e = hipGetLastError();
+    if (e != hipSuccess)
+        return fail_hip(e);
+    if (!ws)
+        return DG_OK;
+    dgk::Params q = p;
+    q.seg_mode = 2;
+    q.ksplit = ks;
+    q.ws = ws;
+    q.ws_rows = p.G * 128;
+    q.tiles_n = p.N / CT::kBN;
+    q.num_tiles = p.G * q.tiles_n * ks;
+    q.tail_slots = q.num_tiles < cus ? q.num_tiles : cus;
+    hipLaunchKernelGGL((dgk::tile_kernel<dgk::kContiguous, CT, 0, SCATTER, true>), dim3(q.tail_slots),
+                       dim3(CT::kThreads), 0, stream, q);
+    if ((e = hipGetLastError()) != hipSuccess)
+        return fail_hip(e);
+    hipLaunchKernelGGL(dgk::seg_tail_reduce_kernel, dim3(128, (unsigned)p.G), dim3(256), 0, stream, q);
+    e = hipGetLastError();
     return e == hipSuccess ? DG_OK : fail_hip(e);
 }
 
@@ -601,10 +637,10 @@ int contiguous_impl(const void *A, int64_t lda, const float *sA, int64_t sa_stri
     if (layout) {
         const bool wide = N % 256 == 0;
         if (token_of_row)
-            return wide ? launch_contiguous_seg<CfgBig, true>(p, dev.cus, (hipStream_t)stream)
-                        : launch_contiguous_seg<CfgDense, true>(p, dev.cus, (hipStream_t)stream);
-        return wide ? launch_contiguous_seg<CfgBig, false>(p, dev.cus, (hipStream_t)stream)
-                    : launch_contiguous_seg<CfgDense, false>(p, dev.cus, (hipStream_t)stream);
+            return wide ? launch_contiguous_seg<CfgBig, CfgWide8, true>(p, dev.cus, (hipStream_t)stream)
+                        : launch_contiguous_seg<CfgDense, CfgNarrow, true>(p, dev.cus, (hipStream_t)stream);
+        return wide ? launch_contiguous_seg<CfgBig, CfgWide8, false>(p, dev.cus, (hipStream_t)stream)
+                    : launch_contiguous_seg<CfgDense, CfgNarrow, false>(p, dev.cus, (hipStream_t)stream);
     }
     if (token_of_row) {
         if (N % 256 == 0)

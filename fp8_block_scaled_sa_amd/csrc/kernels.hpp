@@ -65,6 +65,13 @@ struct Params {
     // Contiguous layout with segment offsets: layout[e] is the first row of
     // expert e's segment (a multiple of 128 rows), layout[G] the rows used.
     const int32_t *layout;
+    // Segment tiles to run: 0 all, 1 the whole 256-row tiles only, 2 the
+    // 128-row tails only, each split over K (at most ksplit slices, chosen by
+    // tail_split for tail_slots workgroups) into work items whose fp32
+    // partials go to ws[slice][128 * tail + row][N] (ws_rows rows per slice).
+    int seg_mode;
+    int ws_rows;
+    int tail_slots;
 };
 
 // One e4m3 x e4m3 -> fp32 MFMA over a 16x16x128 block, C = 0 + A.B.
@@ -303,6 +310,32 @@ __device__ __forceinline__ void wait_stage(int per_stage)
         wait_vmcnt<(SEGW + 2) * LATER>();
 }
 
+// K slices for `tiles` segment-tail tiles on `slots` workgroups: the count in
+// 1..max_split with the lowest estimated time, the smaller on a tie. The
+// estimate, in K-block times of one round: rounds x (K blocks per item + the
+// fp32 partial-tile store) + the reduction's re-read of every slice (each
+// about kTailSliceCost K blocks per round's worth of tiles). The tail kernel
+// and its reduction both call it with the same values.
+// 32-bit arithmetic: tiles < 2 x slots and max_split <= kMaxTailSplit.
+constexpr int kTailSliceCost = 4;
+constexpr int kMaxTailSplit = 8;
+
+__device__ inline int tail_split(int tiles, int nk, int max_split, int slots)
+{
+    int best = 1;
+    int best_cost = INT32_MAX;
+    for (int k = 1; k <= max_split; ++k) {
+        const int items = tiles * k;
+        const int rounds = (items + slots - 1) / slots;
+        const int cost = rounds * ((nk + k - 1) / k + kTailSliceCost) + (kTailSliceCost * items + slots - 1) / slots;
+        if (cost < best_cost) {
+            best = k;
+            best_cost = cost;
+        }
+    }
+    return best;
+}
+
 template <int L, class C, int F = 0, bool SCATTER = false, bool SEG = false>
 __global__ void __launch_bounds__(C::kThreads, 1) tile_kernel(Params p)
 {
@@ -312,7 +345,8 @@ __global__ void __launch_bounds__(C::kThreads, 1) tile_kernel(Params p)
     static_assert(L != kContiguous || BM <= 256, "contiguous tiles span at most two 128-row blocks");
     static_assert(L != kContiguous || C::kWM <= 128, "a wave's rows lie in one 128-row block");
     static_assert(L != kContiguous || BM == 256 || 128 % BM == 0, "contiguous tile rows");
-    static_assert(!SEG || (L == kContiguous && BM == 256), "segment tiles are 256 or 128 rows of one expert");
+    // SEG on 128-row tiles serves the tails-only launch (seg_mode 2)
+    static_assert(!SEG || (L == kContiguous && (BM == 256 || BM == 128)), "segment tiles are 256 or 128 rows of one expert");
 
     __shared__ __attribute__((aligned(1024))) uint8_t smem[C::kSmemBytes];
 
@@ -323,7 +357,6 @@ __global__ void __launch_bounds__(C::kThreads, 1) tile_kernel(Params p)
     const int wm0 = (wave / C::kWavesN) * C::kWM;
     const int wn0 = (wave % C::kWavesN) * C::kWN;
     const int nk_all = p.K >> 7;
-    const int ks = (L == kDense && p.ksplit > 1) ? p.ksplit : 1;
     const int tiles_per_group = p.tiles_m * p.tiles_n;
     const uint32_t smem_base = lds_addr(smem);
     const bool loads_sa = wave < C::kSaLoads;
@@ -344,6 +377,10 @@ __global__ void __launch_bounds__(C::kThreads, 1) tile_kernel(Params p)
             }
         }
     }
+    // K slices per work item; segment tails write every slice to the workspace
+    const bool to_ws = (L == kDense && p.ksplit > 1) || (SEG && p.seg_mode == 2);
+    const int ks = L == kDense ? max(p.ksplit, 1)
+                               : (SEG && p.seg_mode == 2 ? tail_split(seg_half * p.tiles_n, nk_all, p.ksplit, p.tail_slots) : 1);
 
     for (int t = xcd_local_id(blockIdx.x, gridDim.x); t < p.num_tiles; t += gridDim.x) {
         int g = 0, mt, nt;
@@ -351,12 +388,16 @@ __global__ void __launch_bounds__(C::kThreads, 1) tile_kernel(Params p)
         const int slice = t % ks;
         const int kb_lo = (int)((int64_t)slice * nk_all / ks);
         const int nk = (int)((int64_t)(slice + 1) * nk_all / ks) - kb_lo;  // K blocks of this item
-        int seg_m0 = 0, seg_rows = 0, seg_e = 0;
+        int seg_m0 = 0, seg_rows = 0, seg_e = 0, seg_h = 0;
         if constexpr (SEG) {
             mt = 0;
-            if (t < seg_full * p.tiles_n) {
+            // tails-only mode numbers its items from 0 after the whole tiles
+            const int ts = p.seg_mode == 2 ? seg_full * p.tiles_n + t / ks : t;
+            if ((p.seg_mode == 1 && ts >= seg_full * p.tiles_n) || (BM == 128 && ts < seg_full * p.tiles_n))
+                continue;
+            if (ts < seg_full * p.tiles_n) {
                 int ft;
-                tile_coords(t, seg_full, p.tiles_n, C::kGroupM, ft, nt);
+                tile_coords(ts, seg_full, p.tiles_n, C::kGroupM, ft, nt);
                 int before = 0;  // whole tiles of the experts before seg_e
                 for (seg_e = 0; seg_e < p.G; ++seg_e) {
                     const int sz = p.layout[seg_e + 1] - p.layout[seg_e];
@@ -368,10 +409,11 @@ __global__ void __launch_bounds__(C::kThreads, 1) tile_kernel(Params p)
                 seg_m0 = p.layout[seg_e] + 256 * (ft - before);
                 seg_rows = 256;
             } else {
-                const int h = (t - seg_full * p.tiles_n) / p.tiles_n;
+                const int h = (ts - seg_full * p.tiles_n) / p.tiles_n;
                 if (h >= seg_half)
                     continue;  // past the real tiles (uniform over the workgroup)
-                nt = t - seg_full * p.tiles_n - h * p.tiles_n;
+                nt = ts - seg_full * p.tiles_n - h * p.tiles_n;
+                seg_h = h;
                 int seen = 0;
                 for (seg_e = 0; seg_e < p.G; ++seg_e) {
                     const int sz = p.layout[seg_e + 1] - p.layout[seg_e];
@@ -631,13 +673,16 @@ __global__ void __launch_bounds__(C::kThreads, 1) tile_kernel(Params p)
                 return m < limit;
             return m < p.M && p.ids[m] == expert;
         };
-        if (ks > 1) {
+        if (to_ws) {
 #pragma unroll
             for (int i = 0; i < MI; ++i) {
                 const int m = m0 + wm0 + 16 * i + l16;
-                if (!row_ok(m))
+                if (!row_ok(m) || (SEG && m - m0 >= seg_rows))
                     continue;
-                float *wrow = p.ws + ((int64_t)slice * p.M + m) * p.N + n0 + wn0 + 4 * lg;
+                // dense: row m of slice `slice`; segment tails: row 128 h + (m - m0)
+                const int64_t wr = SEG ? (int64_t)slice * p.ws_rows + 128 * seg_h + (m - m0)
+                                       : (int64_t)slice * p.M + m;
+                float *wrow = p.ws + wr * p.N + n0 + wn0 + 4 * lg;
 #pragma unroll
                 for (int j = 0; j < NJ; ++j)
                     *reinterpret_cast<v4f *>(wrow + 16 * j) = acc[i][j];
@@ -713,6 +758,55 @@ __global__ void __launch_bounds__(256) splitk_reduce_kernel(const float *ws, int
     for (int k = 1; k < ksplit; ++k)
         s += *reinterpret_cast<const v4f *>(ws + ((int64_t)k * M + m) * N + c);
     *reinterpret_cast<uint2 *>(D + (int64_t)m * ldd + c) = pack_bf16x4(s);
+}
+
+// Second half of the segment tails split over K: for tail h (the h-th
+// segment whose size is an odd multiple of 128, expert e, rows m0..m0+127),
+// row r goes to D[m0 + r] (or, with row_dst, to row row_dst[m0 + r] of D) when
+// that row belongs to e, as the sum of the slices in order 0, 1, ...
+// One workgroup per tail row (blockIdx.x = r, blockIdx.y = h); each thread
+// takes 4 consecutive columns at a time with every slice's load in flight.
+__global__ void __launch_bounds__(256) seg_tail_reduce_kernel(Params p)
+{
+    const int h = blockIdx.y, r = blockIdx.x;
+    int tails = 0, e = -1;
+    for (int g = 0; g < p.G; ++g) {
+        const int sz = p.layout[g + 1] - p.layout[g];
+        if (sz > 0 && ((sz >> 7) & 1)) {
+            if (tails == h)
+                e = g;
+            ++tails;
+        }
+    }
+    if (e < 0)
+        return;  // fewer tails than the grid allows
+    const int m0 = p.layout[e] + ((p.layout[e + 1] - p.layout[e]) & ~255);
+    const int m = m0 + r;
+    if (m0 < 0 || m >= p.M || p.ids[m] != e)
+        return;
+    int64_t dm = m;
+    if (p.row_dst) {
+        const int t = p.row_dst[m];
+        if (t < 0 || t >= p.dst_rows)
+            return;
+        dm = t;
+    }
+    const int ks = tail_split(tails * p.tiles_n, p.K >> 7, p.ksplit, p.tail_slots);
+    const float *src = p.ws + (int64_t)(128 * h + r) * p.N;
+    const int64_t slice = (int64_t)p.ws_rows * p.N;
+    for (int c = 4 * threadIdx.x; c < p.N; c += 1024) {
+        v4f v[kMaxTailSplit];
+#pragma unroll
+        for (int k = 0; k < kMaxTailSplit; ++k)
+            if (k < ks)
+                v[k] = *reinterpret_cast<const v4f *>(src + k * slice + c);
+        v4f s = v[0];
+#pragma unroll
+        for (int k = 1; k < kMaxTailSplit; ++k)
+            if (k < ks)
+                s += v[k];
+        *reinterpret_cast<uint2 *>(p.D + dm * p.ldd + c) = pack_bf16x4(s);
+    }
 }
 
 // ---------------------------------------------------------------------------

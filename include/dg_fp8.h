@@ -103,6 +103,9 @@ int dg_last_hip_error(void);
  * stream is being captured into a graph nothing is allocated: a call whose
  * stream has no large-enough workspace yet runs without the split (so one
  * eager call on the capture stream beforehand puts the split in the graph).
+ * A captured graph keeps using the workspace it was captured with: a later
+ * call on that stream that needs a larger one frees it, so make the largest
+ * call before capturing, or capture again after such a call.
  * Concurrent calls on different streams use different workspaces. If the
  * allocation fails the call runs without the split.
  *
@@ -179,6 +182,14 @@ int dg_fp8_grouped_gemm_contiguous(const void *A, int64_t lda,
  * experts. Result and other arguments as dg_fp8_grouped_gemm_contiguous;
  * 1 <= G <= 1024. A layout that does not match expert_ids leaves rows
  * unwritten (no fault).
+ * The last 128 rows of the segments may be split over K (at most 8 slices of
+ * at least 4 K blocks, the count chosen on the device from the number of such
+ * segments) when the tails would fill under two rounds of the CUs; those rows
+ * then differ from the unsplit sum only in the grouping of the fp32
+ * additions. The fp32 partials go to the stream's split-K workspace (slices x
+ * G x 128 x N x 4 bytes) under the rules of dg_fp8_gemm_nt: allocated outside
+ * graph capture, so one eager call on a capture stream puts the split in the
+ * graph; without it the call runs unsplit.
  */
 int dg_fp8_grouped_gemm_contiguous_layout(const void *A, int64_t lda,
                                           const float *sA, int64_t sa_stride_m, int64_t sa_stride_kb,

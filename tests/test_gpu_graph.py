@@ -139,12 +139,16 @@ def test_masked_full_size_graph_replay(gpu_device):
         assert_close(got[gs[sel], ms[sel], ns[sel]], ref[sel], "full-size replay")
 
 
-def test_moe_step_graph_replay_with_changing_routing(gpu_device):
+@pytest.mark.parametrize("K,use_layout", [(512, False), (2048, True)])
+def test_moe_step_graph_replay_with_changing_routing(gpu_device, K, use_layout):
     """Routing, quantisation into the layout and the grouped GEMM to token
     order captured once; new routings and activations are copied into the
     captured buffers between replays. Nothing in the step reads sizes on the
-    host, so every replay must equal the eager chain bit for bit."""
-    T, G, N, K = 500, 6, 256, 512
+    host, so every replay must equal the eager chain bit for bit. With the
+    segment offsets at K 2048 the segments' last 128 rows are split over K:
+    one eager step on the capture stream first gives it the workspace, and the
+    slice count chosen on the device follows each routing."""
+    T, G, N = 500, 6, 256
     b, sb = gen.make_grouped_rhs(G, N, K, 821)
     bd, sbd = dev(b), dev(sb)
     M_cap = ops.dg_moe_contiguous_max_rows(T, G)
@@ -164,10 +168,14 @@ def test_moe_step_graph_replay_with_changing_routing(gpu_device):
                                          layout.data_ptr(), M_cap, torch.cuda.current_stream().cuda_stream)
         assert st == 0
         ops.dg_fp8_quantize_1x128_gather(x, tok, q=q, s=s)
-        ops.dg_fp8_grouped_gemm_contiguous_to_tokens(q, s, bd, sbd, ids, tok, T, out=out)
+        ops.dg_fp8_grouped_gemm_contiguous_to_tokens(q, s, bd, sbd, ids, tok, T, layout=layout if use_layout else None,
+                                                     out=out)
 
     stream = torch.cuda.Stream()
     stream.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(stream):
+        step()
+    torch.cuda.synchronize()
     graph = torch.cuda.CUDAGraph()
     with torch.cuda.graph(graph, stream=stream):
         step()
