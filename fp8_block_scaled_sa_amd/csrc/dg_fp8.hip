@@ -148,7 +148,9 @@ using CfgBig = dgk::TileCfg<256, 256, 2, 4, 2, 4>;  // 2 stages of 66 KB; N % 25
 using CfgBigStreamB = dgk::TileCfg<256, 256, 2, 4, 2, 4, true>;
 using CfgWide = dgk::TileCfg<128, 256, 2, 2, 3, 8>;
 using CfgNarrow = dgk::TileCfg<128, 128, 2, 2, 4, 8>;
-using CfgWide8 = dgk::TileCfg<128, 256, 2, 4, 2, 4>;  // segment tails next to CfgBig (8 waves, 8% faster than 4 there)
+// Segment tails next to CfgBig: 8 waves and 3 stages of 50 KB. 8 waves were
+// 8% faster there than CfgWide's 4, and 3 stages another 2% (5 us) than 2.
+using CfgTail = dgk::TileCfg<128, 256, 2, 4, 3, 4>;
 
 // Optional override of the kernel choice, read once: DG_TILE=<index>, for
 // measurements. 1, 2, 4: dense on 256x128 (4 waves), 128x128 or 256x128 tiles
@@ -637,9 +639,9 @@ int contiguous_impl(const void *A, int64_t lda, const float *sA, int64_t sa_stri
     if (layout) {
         const bool wide = N % 256 == 0;
         if (token_of_row)
-            return wide ? launch_contiguous_seg<CfgBig, CfgWide8, true>(p, dev.cus, (hipStream_t)stream)
+            return wide ? launch_contiguous_seg<CfgBig, CfgTail, true>(p, dev.cus, (hipStream_t)stream)
                         : launch_contiguous_seg<CfgDense, CfgNarrow, true>(p, dev.cus, (hipStream_t)stream);
-        return wide ? launch_contiguous_seg<CfgBig, CfgWide8, false>(p, dev.cus, (hipStream_t)stream)
+        return wide ? launch_contiguous_seg<CfgBig, CfgTail, false>(p, dev.cus, (hipStream_t)stream)
                     : launch_contiguous_seg<CfgDense, CfgNarrow, false>(p, dev.cus, (hipStream_t)stream);
     }
     if (token_of_row) {
