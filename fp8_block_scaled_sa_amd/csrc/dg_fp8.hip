@@ -962,12 +962,7 @@ int dg_moe_route_contiguous(const int32_t *expert_of_token, int64_t T, int64_t G
     p.expert_of_token = expert_of_token;
     p.T = (int)T; p.G = (int)G; p.M_cap = (int)M_cap;
     p.row_of_token = row_of_token; p.expert_ids = expert_ids; p.token_of_row = token_of_row; p.layout = layout;
-    if (G <= 64)
-        hipLaunchKernelGGL(dgm::route_contiguous_kernel<true>, dim3(1), dim3(dgm::kRouteThreads), 0,
-                           (hipStream_t)stream, p);
-    else
-        hipLaunchKernelGGL(dgm::route_contiguous_kernel<false>, dim3(1), dim3(dgm::kRouteThreads), 0,
-                           (hipStream_t)stream, p);
+    hipLaunchKernelGGL(dgm::route_contiguous_kernel, dim3(1), dim3(dgm::kRouteThreads), 0, (hipStream_t)stream, p);
     const hipError_t e = hipGetLastError();
     return e == hipSuccess ? DG_OK : fail_hip(e);
 }

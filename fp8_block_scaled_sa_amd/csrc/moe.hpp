@@ -12,13 +12,14 @@
 //
 // Routing is a stable counting sort in one workgroup of 16 waves. Each wave
 // owns a contiguous range of tokens, loads up to 16 chunks of 64 at once and
-// takes the chunks one after another; inside such
-// a chunk, the lanes holding one expert are found with a ballot on the first
-// remaining lane's id, so a chunk costs one round per distinct expert in it.
-// Pass 1 counts per (wave, expert); an exclusive prefix over the waves and a
-// scan over the padded segment sizes give every token's row in pass 2. No
-// atomics: the result is the same on every run. With at most 64 experts the
-// per-wave counts stay in registers (lane j: expert j) during both passes.
+// takes the chunks one after another. Inside a chunk, every lane finds the
+// lanes that hold its own expert with one ballot per bit of the expert id (a
+// multisplit by key bits: Ashkiani et al., "GPU Multisplit", PPoPP 2016), so
+// a chunk costs ceil(log2 G) ballots whatever its mix of experts; a lane's
+// rank among them is the count of such lanes below it. Pass 1 counts per
+// (wave, expert) in LDS; an exclusive prefix over the waves and a scan over
+// the padded segment sizes give every token's row in pass 2. No atomics: the
+// result is the same on every run.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -55,10 +56,20 @@ __device__ __forceinline__ void load_experts(const RouteParams &p, int base, int
     }
 }
 
-// SMALL (G <= 64): lane j of each wave keeps expert j's count in a register,
-// read and updated with v_readlane / a lane-predicated add, so a ballot round
-// does no LDS traffic. Otherwise the counts live in LDS.
-template <bool SMALL>
+// Lanes of the wave whose expert equals this lane's (e >= 0; only lanes with
+// e >= 0 take part): ANDs the ballot of each id bit, or of its complement,
+// over the `bits` bits that ids in [0, G) use. Uniform over the wave.
+__device__ __forceinline__ uint64_t same_expert(int e, int bits)
+{
+    uint64_t same = __ballot(e >= 0);
+    for (int b = 0; b < bits; ++b) {
+        const bool set = (e >> b) & 1;
+        const uint64_t m = __ballot(set);
+        same &= set ? m : ~m;
+    }
+    return same;
+}
+
 __global__ __launch_bounds__(kRouteThreads) void route_contiguous_kernel(RouteParams p)
 {
     __shared__ int cnt[kRouteWaves][kMaxExperts];  // per-wave counts, then per-wave running offsets
@@ -72,7 +83,8 @@ __global__ __launch_bounds__(kRouteThreads) void route_contiguous_kernel(RoutePa
 
     const int chunk = (p.T + kRouteWaves - 1) / kRouteWaves;
     const int t0 = min(p.T, w * chunk), t1 = min(p.T, t0 + chunk);
-    int mine = 0;  // SMALL: this wave's count of expert `lane`
+    const int bits = p.G > 1 ? 32 - __clz(p.G - 1) : 0;
+    const uint64_t below = (1ull << lane) - 1;  // lanes under this one
     for (int sc = t0; sc < t1; sc += 64 * kChunks) {
         int ex[kChunks];
         load_experts(p, sc, t1, lane, ex);
@@ -81,23 +93,13 @@ __global__ __launch_bounds__(kRouteThreads) void route_contiguous_kernel(RoutePa
             if (sc + 64 * c >= t1)
                 break;
             const int e = ex[c];
-            uint64_t todo = __ballot(e >= 0);
-            while (todo) {
-                const int leader = __ffsll((unsigned long long)todo) - 1;
-                const int el = __builtin_amdgcn_readlane(e, leader);
-                const uint64_t same = __ballot(e == el);
-                if (SMALL) {
-                    if (lane == el)
-                        mine += __popcll(same);
-                } else if (lane == leader) {
-                    cnt[w][el] += __popcll(same);
-                }
-                todo &= ~same;
-            }
+            const uint64_t same = same_expert(e, bits);
+            // the lowest lane of each expert adds the chunk's count (distinct
+            // addresses within the chunk; this wave's LDS operations stay in order)
+            if (e >= 0 && (same & below) == 0)
+                cnt[w][e] += __popcll(same);
         }
     }
-    if (SMALL && lane < p.G)
-        cnt[w][lane] = mine;
     __syncthreads();
 
     const int e = threadIdx.x;  // G <= kMaxExperts == kRouteThreads: one expert per thread
@@ -139,8 +141,6 @@ __global__ __launch_bounds__(kRouteThreads) void route_contiguous_kernel(RoutePa
         p.token_of_row[r] = -1;
     }
 
-    // SMALL: lane j holds the next row of expert j for this wave
-    int next = (SMALL && lane < p.G) ? seg[lane] + cnt[w][lane] : 0;
     for (int sc = t0; sc < t1; sc += 64 * kChunks) {
         int ex[kChunks];
         load_experts(p, sc, t1, lane, ex);
@@ -150,26 +150,16 @@ __global__ __launch_bounds__(kRouteThreads) void route_contiguous_kernel(RoutePa
                 break;
             const int t = sc + 64 * c + lane;
             const int e = ex[c];
-            uint64_t todo = __ballot(e >= 0);
+            const uint64_t same = same_expert(e, bits);
             int row = -1;
-            while (todo) {
-                const int leader = __ffsll((unsigned long long)todo) - 1;
-                const int el = __builtin_amdgcn_readlane(e, leader);
-                const uint64_t same = __ballot(e == el);
-                const int rank = __popcll(same & ((1ull << lane) - 1));
-                if (SMALL) {
-                    const int base = __builtin_amdgcn_readlane(next, el);
-                    if (e == el)
-                        row = base + rank;
-                    if (lane == el)
-                        next += __popcll(same);
-                } else {
-                    if (e == el)
-                        row = seg[el] + cnt[w][el] + rank;
-                    if (lane == leader)
-                        cnt[w][el] += __popcll(same);
-                }
-                todo &= ~same;
+            if (e >= 0) {
+                // cnt holds this wave's running offset within expert e's
+                // segment; the chunk's lanes of e take the next rows in lane
+                // order, and the lowest of them moves the offset on
+                const int off = cnt[w][e];
+                row = seg[e] + off + __popcll(same & below);
+                if ((same & below) == 0)
+                    cnt[w][e] = off + __popcll(same);
             }
             if (t < t1) {
                 p.row_of_token[t] = row;

@@ -27,9 +27,15 @@ def route_both(e, G, M_cap=None):
 @pytest.mark.parametrize("T,G,seed", [
     (8192, 8, 403),      # the contiguous MoE workload's routing
     (1000, 32, 1), (64, 256, 2), (5, 3, 3), (300, 1, 4), (4096, 1024, 5), (777, 7, 6), (65, 64, 7),
+    (20000, 100, 8), (8192, 2, 9), (3000, 65, 10), (10000, 1000, 11),
 ])
 def test_route_matches_oracle(gpu_device, T, G, seed):
-    e = np.random.Generator(np.random.PCG64(seed)).choice(G, T).astype(np.int32)
+    rng = np.random.Generator(np.random.PCG64(seed))
+    # seeds from 8 on: skewed expert loads (Dirichlet weights), some ids dropped
+    p = rng.dirichlet(np.full(G, 0.3)) if seed >= 8 else None
+    e = rng.choice(G, T, p=p).astype(np.int32)
+    if seed >= 8:
+        e[rng.random(T) < 0.02] = -1
     got, ref = route_both(e, G)
     for name, g, r in zip(("row_of_token", "expert_ids", "token_of_row", "layout"), got, ref):
         assert np.array_equal(g, r), name
