@@ -105,3 +105,48 @@ def test_masked_fuzz(gpu_device, seed):
         assert np.all(got[g, cnt:] == SENTINEL), "seed %d group %d: rows past the count written" % (seed, g)
         if cnt:
             assert_close(got[g, :cnt], ref[g, :cnt], "seed %d group %d" % (seed, g))
+
+
+MAX_LAYOUT_MACS = 1_500_000_000
+
+
+@pytest.mark.parametrize("seed", range(30))
+def test_contiguous_layout_fuzz(gpu_device, seed):
+    """Segment-tiled contiguous GEMM (segment offsets given) on seeded shapes:
+    skewed expert loads, K up to 4096 so the segments' last 128 rows are
+    split over K with the slice count the device picks from the number of
+    such segments; every fourth case writes to token order."""
+    rng = np.random.default_rng(4000 + seed)
+    while True:
+        G = int(rng.integers(1, 17))
+        T = int(rng.integers(1, 2500))
+        N = 256 * int(rng.integers(1, 5))
+        K = 128 * int(rng.choice([rng.integers(1, 9), rng.integers(8, 33)]))
+        if T * N * K <= MAX_LAYOUT_MACS:
+            break
+    e = rng.choice(G, T, p=rng.dirichlet(np.ones(G) * 0.6)).astype(np.int32)
+    c = gen.make_contiguous(G, T, N, K, 4100 + seed, 4200 + seed, 0, expert_of_token=e)
+    layout = gen.segment_layout(c.counts).astype(np.int32)
+    assert layout[-1] == c.M_total
+    args = (dev(c.a), dev(c.sa_t).t(), dev(c.b), dev(c.sb), dev(c.ids))
+    ref = oracle.grouped_contiguous(c.a, c.sa_t.T, c.b, c.sb, c.ids, np.full((c.M_total, N), SENTINEL, np.uint16))
+    valid = c.ids >= 0
+    what = "seed %d: G=%d T=%d N=%d K=%d" % (seed, G, T, N, K)
+    if seed % 4 == 3:
+        tok = c.token_of_row.astype(np.int32)
+        out = sentinel_bf16((T, N))
+        ops.dg_fp8_grouped_gemm_contiguous_to_tokens(args[0], args[1], args[2], args[3], args[4], dev(tok), T,
+                                                     layout=dev(layout), out=out)
+        torch.cuda.synchronize()
+        got = bits(out)
+        assert_close(got[tok[valid]], ref[valid], what)
+        routed = np.zeros(T, bool)
+        routed[tok[valid]] = True
+        assert np.all(got[~routed] == SENTINEL), what
+        return
+    d = sentinel_bf16((c.M_total, N))
+    ops.dg_fp8_grouped_gemm_contiguous_layout(*args, dev(layout), d=d)
+    torch.cuda.synchronize()
+    got = bits(d)
+    assert np.all(got[~valid] == SENTINEL), "%s: padding rows written" % what
+    assert_close(got[valid], ref[valid], what)
