@@ -207,7 +207,8 @@ int dg_fp8_grouped_gemm_contiguous_layout(const void *A, int64_t lda,
  * This folds dg_moe_unpermute into the GEMM's epilogue.
  *   token_of_row [M_total] int32 (device), as written by dg_moe_route_contiguous
  *   layout [G + 1] int32 (device) or NULL: segment offsets as in
- *   dg_fp8_grouped_gemm_contiguous_layout (then tiles follow the segments)
+ *   dg_fp8_grouped_gemm_contiguous_layout (then tiles follow the segments,
+ *   and the segments' last 128 rows may be split over K as described there)
  *   out [T, N] bf16, row stride ldo: rows of tokens that no row names (dropped
  *   tokens) are NOT written.
  * Precondition: no token appears twice in token_of_row (the routing call
