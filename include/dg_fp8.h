@@ -31,8 +31,9 @@
  *     keeps one past return.
  *   - `stream` is a hipStream_t (NULL = the legacy default stream). The call
  *     validates its arguments on the host, enqueues its kernels and returns.
- *     It allocates nothing and does not synchronise, with one exception in
- *     dg_fp8_gemm_nt (see there).
+ *     It allocates nothing and does not synchronise, except for the split-K
+ *     workspace that dg_fp8_gemm_nt (and _fmt) and the segment-tiled grouped
+ *     GEMM (_layout, _to_tokens with a layout) share (see dg_fp8_gemm_nt).
  *   - Strides are in elements. e4m3 is one byte, so A/B strides are also byte
  *     strides; D strides count bf16 elements. Scale tables are addressed
  *     logically through explicit strides: sA[m, kb] = sA[m*sa_stride_m +
@@ -46,7 +47,7 @@
  *   - D must not overlap A, B, sA, sB or the routing arrays.
  *   - Results are deterministic: no atomics, a fixed reduction order.
  *   - Thread-safe; the global state is a per-device property cache and the
- *     split-K workspaces of dg_fp8_gemm_nt.
+ *     per-stream split-K workspaces.
  *
  * Errors: every error is detected on the host before anything is enqueued,
  * and D is left untouched. DG_ERR_HIP reports a failed launch; the HIP error
