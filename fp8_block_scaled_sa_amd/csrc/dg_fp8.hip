@@ -66,20 +66,22 @@ struct Workspace {
     float *ptr = nullptr;
     size_t bytes = 0;
 };
-std::map<std::pair<int, hipStream_t>, Workspace> g_workspaces;
+using WorkspaceMap = std::map<std::pair<int, hipStream_t>, Workspace>;
+WorkspaceMap g_workspaces;
+WorkspaceMap g_aux;  // segment offsets derived on the device (a few KB per stream)
 std::mutex g_workspaces_mu;
 
 // A buffer of at least `bytes` for `stream`, or nullptr (allocation failed,
 // or the stream is being captured into a graph and has no large-enough
 // buffer yet: nothing is allocated or synchronised during a capture).
 // Growing waits for the stream, whose queued kernels may still use the old one.
-float *stream_workspace(hipStream_t stream, size_t bytes)
+float *stream_buffer(WorkspaceMap &m, hipStream_t stream, size_t bytes)
 {
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess)
         return nullptr;
     std::lock_guard<std::mutex> lk(g_workspaces_mu);
-    Workspace &w = g_workspaces[{dev, stream}];
+    Workspace &w = m[{dev, stream}];
     if (w.bytes >= bytes)
         return w.ptr;
     hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
@@ -102,6 +104,9 @@ float *stream_workspace(hipStream_t stream, size_t bytes)
     w.bytes = want;
     return w.ptr;
 }
+
+float *stream_workspace(hipStream_t stream, size_t bytes) { return stream_buffer(g_workspaces, stream, bytes); }
+int32_t *stream_aux(hipStream_t stream, size_t bytes) { return (int32_t *)stream_buffer(g_aux, stream, bytes); }
 
 bool aligned(const void *p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
 
@@ -159,7 +164,8 @@ using CfgTail = dgk::TileCfg<128, 256, 2, 4, 3, 4>;
 // decode kernels up to M = 16 / all older decode kernels up to 64; 15:
 // split-K always on 256-wide tiles;
 // 16: no split-K; 18: no cut of a partly filled last round of 256x256 tiles;
-// 23: segment tails not split over K;
+// 23: segment tails not split over K; 24: the contiguous call without
+// segment offsets stays on the uniform grid (no offsets derived on the device);
 // 2, 3, 4 also pick the contiguous layout's tile shape.
 int tile_override()
 {
@@ -643,6 +649,31 @@ int contiguous_impl(const void *A, int64_t lda, const float *sA, int64_t sa_stri
                         : launch_contiguous_seg<CfgDense, CfgNarrow, true>(p, dev.cus, (hipStream_t)stream);
         return wide ? launch_contiguous_seg<CfgBig, CfgTail, false>(p, dev.cus, (hipStream_t)stream)
                     : launch_contiguous_seg<CfgDense, CfgNarrow, false>(p, dev.cus, (hipStream_t)stream);
+    }
+    // Only the ids given: derive the segment offsets on the device and tile
+    // along them (e4m3, 256-wide tiles, G <= 1024, at most 4096 blocks of 128
+    // rows, outside graph capture unless the stream's buffer exists). The
+    // uniform-grid launch below then runs only if the ids' experts were not
+    // in ascending order, which the derivation flags.
+    const int ov = tile_override();  // 24: no derivation; 2, 3, 4 force the uniform grid's tile shape
+    if (!fmt && N % 256 == 0 && G <= dgm::kMaxExperts && M_total / 128 <= dgm::kDeriveMaxBlocks && ov != 24 &&
+        ov != 2 && ov != 3 && ov != 4) {
+        int32_t *aux = stream_aux((hipStream_t)stream, (size_t)(G + 2) * sizeof(int32_t));
+        if (aux) {
+            dgm::DeriveParams dp = {expert_ids, (int)M_total, (int)G, aux, aux + G + 1};
+            hipLaunchKernelGGL(dgm::derive_layout_kernel, dim3(1), dim3(dgm::kRouteThreads), 0, (hipStream_t)stream,
+                               dp);
+            const hipError_t e = hipGetLastError();
+            if (e != hipSuccess)
+                return fail_hip(e);
+            dgk::Params q = p;
+            q.layout = aux;
+            st = token_of_row ? launch_contiguous_seg<CfgBig, CfgTail, true>(q, dev.cus, (hipStream_t)stream)
+                              : launch_contiguous_seg<CfgBig, CfgTail, false>(q, dev.cus, (hipStream_t)stream);
+            if (st != DG_OK)
+                return st;
+            p.gate = aux + G + 1;
+        }
     }
     if (token_of_row) {
         if (N % 256 == 0)

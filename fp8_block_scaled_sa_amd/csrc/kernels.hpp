@@ -72,6 +72,10 @@ struct Params {
     int seg_mode;
     int ws_rows;
     int tail_slots;
+    // Contiguous layout on the uniform grid: when set, the launch does
+    // nothing unless *gate != 0 (segment offsets derived on the device were
+    // not usable, so this launch covers the rows instead).
+    const int32_t *gate;
 };
 
 // One e4m3 x e4m3 -> fp32 MFMA over a 16x16x128 block, C = 0 + A.B.
@@ -350,6 +354,10 @@ __global__ void __launch_bounds__(C::kThreads, 1) tile_kernel(Params p)
 
     __shared__ __attribute__((aligned(1024))) uint8_t smem[C::kSmemBytes];
 
+    if constexpr (L == kContiguous && !SEG) {
+        if (p.gate && *p.gate == 0)
+            return;  // uniform over the grid
+    }
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);

@@ -206,4 +206,107 @@ __global__ __launch_bounds__(64 * kUnpermuteWaves) void unpermute_kernel(Unpermu
         *(u32x4m *)(dst + n) = *(const u32x4m *)(src + n);
 }
 
+// Segment offsets for the contiguous grouped GEMM derived from its expert ids
+// alone, so that a call given only the ids can tile along the segments. A
+// 128-row block's expert is the largest id in [0, G) among its rows (-1 for a
+// block of padding only), as the GEMM itself defines it. When the non-padding
+// block experts never decrease, layout[e] is the first row of the first block
+// whose expert is >= e and layout[G] the end of the last non-padding block:
+// each segment then holds its expert's blocks and the padding blocks after
+// them, and the GEMM writes exactly the rows it writes on the uniform grid.
+// Otherwise every offset is 0 (no segment tiles) and *use_grid = 1, which
+// gates the uniform-grid launch that follows; else *use_grid = 0.
+// One workgroup of 16 waves; nb = M / 128 <= kDeriveMaxBlocks.
+constexpr int kDeriveMaxBlocks = 4096;
+
+struct DeriveParams {
+    const int32_t *ids;  // [M]
+    int M, G;
+    int32_t *layout;     // [G + 1]
+    int32_t *use_grid;   // [1]
+};
+
+__global__ __launch_bounds__(kRouteThreads) void derive_layout_kernel(DeriveParams p)
+{
+    __shared__ int bexp[kDeriveMaxBlocks];  // block experts, then their prefix maximum
+    __shared__ int s_ok, s_end;
+    const int lane = threadIdx.x & 63;
+    const int w = threadIdx.x >> 6;
+    const int nb = p.M >> 7;
+    for (int b = w; b < nb; b += kRouteWaves) {
+        int e0 = p.ids[128 * b + lane], e1 = p.ids[128 * b + 64 + lane];
+        e0 = (e0 >= 0 && e0 < p.G) ? e0 : -1;
+        e1 = (e1 >= 0 && e1 < p.G) ? e1 : -1;
+        int e = max(e0, e1);
+        for (int o = 32; o > 0; o >>= 1)
+            e = max(e, __shfl_xor(e, o));
+        if (lane == 0)
+            bexp[b] = e;
+    }
+    __syncthreads();
+    if (w == 0) {
+        // lane l takes blocks [l * chunk, (l + 1) * chunk)
+        const int chunk = (nb + 63) / 64;
+        const int b0 = min(nb, lane * chunk), b1 = min(nb, b0 + chunk);
+        int run = -1, first = -1, last = -1;
+        bool ok = true;
+        for (int b = b0; b < b1; ++b) {
+            const int e = bexp[b];
+            if (e >= 0) {
+                ok = ok && e >= run;
+                if (first < 0)
+                    first = e;
+                last = b;
+            }
+            run = max(run, e);
+        }
+        // maximum over the lanes below (exclusive prefix maximum)
+        int below = run;
+        for (int o = 1; o < 64; o <<= 1) {
+            const int v = __shfl_up(below, o);
+            if (lane >= o)
+                below = max(below, v);
+        }
+        below = __shfl_up(below, 1);
+        if (lane == 0)
+            below = -1;
+        ok = ok && (first < 0 || first >= below);
+        int end = last;
+        for (int o = 32; o > 0; o >>= 1)
+            end = max(end, __shfl_xor(end, o));
+        const bool all_ok = __ballot(!ok) == 0;
+        // prefix maximum in place
+        int m = below;
+        for (int b = b0; b < b1; ++b) {
+            m = max(m, bexp[b]);
+            bexp[b] = m;
+        }
+        if (lane == 0) {
+            s_ok = all_ok ? 1 : 0;
+            s_end = end + 1;  // blocks up to the last non-padding one
+        }
+    }
+    __syncthreads();
+    const bool ok = s_ok != 0;
+    for (int e = threadIdx.x; e <= p.G; e += kRouteThreads) {
+        int v = 0;
+        if (ok) {
+            // first block whose prefix maximum is >= e (the prefix maximum
+            // never decreases), capped at the end of the last non-padding block
+            int lo = 0, hi = nb;
+            while (lo < hi) {
+                const int mid = (lo + hi) >> 1;
+                if (bexp[mid] >= e)
+                    hi = mid;
+                else
+                    lo = mid + 1;
+            }
+            v = 128 * min(e == p.G ? s_end : lo, s_end);
+        }
+        p.layout[e] = v;
+    }
+    if (threadIdx.x == 0)
+        *p.use_grid = ok ? 0 : 1;
+}
+
 }  // namespace dgm

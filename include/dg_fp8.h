@@ -33,7 +33,8 @@
  *     validates its arguments on the host, enqueues its kernels and returns.
  *     It allocates nothing and does not synchronise, except for the split-K
  *     workspace that dg_fp8_gemm_nt (and _fmt) and the segment-tiled grouped
- *     GEMM (_layout, _to_tokens with a layout) share (see dg_fp8_gemm_nt).
+ *     GEMMs share (see dg_fp8_gemm_nt), and the small buffer of segment
+ *     offsets that dg_fp8_grouped_gemm_contiguous derives (see there).
  *   - Strides are in elements. e4m3 is one byte, so A/B strides are also byte
  *     strides; D strides count bf16 elements. Scale tables are addressed
  *     logically through explicit strides: sA[m, kb] = sA[m*sa_stride_m +
@@ -47,7 +48,7 @@
  *   - D must not overlap A, B, sA, sB or the routing arrays.
  *   - Results are deterministic: no atomics, a fixed reduction order.
  *   - Thread-safe; the global state is a per-device property cache and the
- *     per-stream split-K workspaces.
+ *     per-stream split-K workspaces and offset buffers.
  *
  * Errors: every error is detected on the host before anything is enqueued,
  * and D is left untouched. DG_ERR_HIP reports a failed launch; the HIP error
@@ -161,6 +162,16 @@ int dg_fp8_gemm_nt_fmt(const void *A, int a_fmt, int64_t lda,
  * Layout contract: M_total % 128 == 0 and within every aligned 128-row block
  * all ids in [0, G) are equal (segments padded to 128). A block's expert is
  * the largest id in the block; a row whose id differs from it is not written.
+ * Tiling: for e4m3 operands with N % 256 == 0, G <= 1024 and at most 4096
+ * blocks of 128 rows, a one-workgroup kernel first derives each expert's
+ * segment offsets from expert_ids on the device, into a per-stream buffer of
+ * (G + 2) int32 kept by the library (allocated like the split-K workspace of
+ * dg_fp8_gemm_nt, never during graph capture). The GEMM then tiles along the
+ * segments as dg_fp8_grouped_gemm_contiguous_layout does, tails split over K
+ * included. If the block experts are not in ascending order (padding blocks
+ * anywhere are fine), the derivation says so on the device and a uniform-grid
+ * launch covers the rows instead. Either way the rows written are the same;
+ * their values differ only in the grouping of the fp32 sums of split tails.
  */
 int dg_fp8_grouped_gemm_contiguous(const void *A, int64_t lda,
                                    const float *sA, int64_t sa_stride_m, int64_t sa_stride_kb,

@@ -137,3 +137,48 @@ def test_layout_that_does_not_fit_writes_nothing(gpu_device, kind):
         layout = (-4096 + 256 * np.arange(G + 1)).astype(np.int32)
     _, seg = run_both(c, layout)
     assert np.all(seg == SENTINEL)
+
+
+def blocks_reordered(c, order_blocks):
+    """The contiguous problem c with its 128-row blocks taken in the order given
+    (a list of block indexes, -1 for an extra block of padding)."""
+    a = np.zeros((128 * len(order_blocks), c.K), np.uint8)
+    sa_t = np.zeros((c.K // 128, 128 * len(order_blocks)), np.float32)
+    ids = np.full(128 * len(order_blocks), -1, np.int32)
+    for i, b in enumerate(order_blocks):
+        if b >= 0:
+            a[128 * i:128 * i + 128] = c.a[128 * b:128 * b + 128]
+            sa_t[:, 128 * i:128 * i + 128] = c.sa_t[:, 128 * b:128 * b + 128]
+            ids[128 * i:128 * i + 128] = c.ids[128 * b:128 * b + 128]
+        else:
+            sa_t[:, 128 * i:128 * i + 128] = 1.0
+    return a, sa_t, ids
+
+
+@pytest.mark.parametrize("case", ["descending", "interleaved", "padding_blocks"])
+def test_plain_call_any_block_order(gpu_device, case):
+    """The call given only the ids derives the segment offsets on the device
+    when the experts ascend (padding blocks anywhere allowed) and falls back to
+    the uniform grid otherwise; either way every valid row matches the oracle
+    and padding rows stay untouched."""
+    G, T, N, K = 5, 900, 256, 1024
+    e = np.random.default_rng(21).choice(G, T).astype(np.int32)
+    c = gen.make_contiguous(G, T, N, K, 961, 962, 0, expert_of_token=e)
+    layout = layout_of(c.counts)
+    seg_blocks = [list(range(layout[g] // 128, layout[g + 1] // 128)) for g in range(G)]
+    if case == "descending":
+        order = [b for g in reversed(range(G)) for b in seg_blocks[g]]
+    elif case == "interleaved":
+        order = [b for g in (1, 0, 2, 4, 3) for b in seg_blocks[g]]
+    else:
+        order = [-1, -1] + [b for g in range(G) for b in seg_blocks[g] + ([-1] if g % 2 else [])] + [-1, -1, -1]
+    a, sa_t, ids = blocks_reordered(c, order)
+    M = len(ids)
+    d = sentinel_bf16((M, N))
+    ops.dg_fp8_grouped_gemm_contiguous(dev(a), dev(sa_t).t(), dev(c.b), dev(c.sb), dev(ids), d=d)
+    torch.cuda.synchronize()
+    got = bits(d)
+    ref = oracle.grouped_contiguous(a, sa_t.T, c.b, c.sb, ids, np.full((M, N), SENTINEL, np.uint16))
+    valid = ids >= 0
+    assert np.all(got[~valid] == SENTINEL), case
+    assert_close(got[valid], ref[valid], "plain call, blocks %s" % case)
