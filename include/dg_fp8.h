@@ -220,7 +220,9 @@ int dg_fp8_grouped_gemm_contiguous_layout(const void *A, int64_t lda,
  *   token_of_row [M_total] int32 (device), as written by dg_moe_route_contiguous
  *   layout [G + 1] int32 (device) or NULL: segment offsets as in
  *   dg_fp8_grouped_gemm_contiguous_layout (then tiles follow the segments,
- *   and the segments' last 128 rows may be split over K as described there)
+ *   and the segments' last 128 rows may be split over K as described there);
+ *   with NULL the offsets are derived from expert_ids on the device as in
+ *   dg_fp8_grouped_gemm_contiguous
  *   out [T, N] bf16, row stride ldo: rows of tokens that no row names (dropped
  *   tokens) are NOT written.
  * Precondition: no token appears twice in token_of_row (the routing call
