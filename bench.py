@@ -322,7 +322,7 @@ def cpu_baseline(name, p, byts, min_seconds=10.0):
     workload, repeated until at least min_seconds of work have run (one pass if
     a single pass takes longer)."""
     import oracle
-    threads = min(16, len(os.sched_getaffinity(0)))   # the GPU box grants 16 cores per GPU
+    threads = min(16, len(os.sched_getaffinity(0)))   # at most 16 host cores per GPU
     passes = 0
     t0 = time.perf_counter()
     while True:
