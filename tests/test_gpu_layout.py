@@ -145,14 +145,16 @@ def blocks_reordered(c, order_blocks):
     a = np.zeros((128 * len(order_blocks), c.K), np.uint8)
     sa_t = np.zeros((c.K // 128, 128 * len(order_blocks)), np.float32)
     ids = np.full(128 * len(order_blocks), -1, np.int32)
+    tok = np.full(128 * len(order_blocks), -1, np.int32)
     for i, b in enumerate(order_blocks):
         if b >= 0:
             a[128 * i:128 * i + 128] = c.a[128 * b:128 * b + 128]
             sa_t[:, 128 * i:128 * i + 128] = c.sa_t[:, 128 * b:128 * b + 128]
             ids[128 * i:128 * i + 128] = c.ids[128 * b:128 * b + 128]
+            tok[128 * i:128 * i + 128] = c.token_of_row[128 * b:128 * b + 128]
         else:
             sa_t[:, 128 * i:128 * i + 128] = 1.0
-    return a, sa_t, ids
+    return a, sa_t, ids, tok
 
 
 @pytest.mark.parametrize("case", ["descending", "interleaved", "padding_blocks"])
@@ -172,13 +174,18 @@ def test_plain_call_any_block_order(gpu_device, case):
         order = [b for g in (1, 0, 2, 4, 3) for b in seg_blocks[g]]
     else:
         order = [-1, -1] + [b for g in range(G) for b in seg_blocks[g] + ([-1] if g % 2 else [])] + [-1, -1, -1]
-    a, sa_t, ids = blocks_reordered(c, order)
+    a, sa_t, ids, tok = blocks_reordered(c, order)
     M = len(ids)
+    args = (dev(a), dev(sa_t).t(), dev(c.b), dev(c.sb), dev(ids))
     d = sentinel_bf16((M, N))
-    ops.dg_fp8_grouped_gemm_contiguous(dev(a), dev(sa_t).t(), dev(c.b), dev(c.sb), dev(ids), d=d)
+    ops.dg_fp8_grouped_gemm_contiguous(*args, d=d)
+    out = sentinel_bf16((T, N))
+    ops.dg_fp8_grouped_gemm_contiguous_to_tokens(*args, dev(tok), T, out=out)
     torch.cuda.synchronize()
     got = bits(d)
     ref = oracle.grouped_contiguous(a, sa_t.T, c.b, c.sb, ids, np.full((M, N), SENTINEL, np.uint16))
     valid = ids >= 0
     assert np.all(got[~valid] == SENTINEL), case
     assert_close(got[valid], ref[valid], "plain call, blocks %s" % case)
+    # the token-order call takes the same path: its rows equal the plain call's
+    assert np.array_equal(bits(out)[tok[valid]], got[valid]), case
