@@ -189,3 +189,60 @@ def test_plain_call_any_block_order(gpu_device, case):
     assert_close(got[valid], ref[valid], "plain call, blocks %s" % case)
     # the token-order call takes the same path: its rows equal the plain call's
     assert np.array_equal(bits(out)[tok[valid]], got[valid]), case
+
+
+def plain_ids_case(kind):
+    """(ids, G, K) for the plain-call edge cases."""
+    rng = np.random.default_rng(31)
+    if kind == "all_padding":
+        return np.full(512, -1, np.int32), 4, 256
+    if kind == "one_expert":
+        ids = np.full(640, 0, np.int32)
+        ids[600:] = -1
+        return ids, 1, 1024
+    if kind == "last_expert_only":
+        ids = np.full(768, -1, np.int32)
+        ids[256:700] = 5
+        return ids, 6, 1024
+    if kind == "ids_out_of_range":
+        ids = np.repeat(np.arange(4, dtype=np.int32), 256)
+        ids[rng.choice(len(ids), 40, replace=False)] = rng.choice([-3, 4, 7, 1000], 40)
+        return ids, 4, 512
+    if kind == "many_blocks":
+        counts = rng.multinomial(120000, np.ones(16) / 16)
+        ids = np.concatenate([np.r_[np.full(c, g), np.full((-c) % 128, -1)] for g, c in enumerate(counts)])
+        return ids.astype(np.int32), 16, 256
+    if kind == "no_split_k128":
+        ids = np.repeat(np.arange(3, dtype=np.int32), 384)
+        return ids, 3, 128
+    raise ValueError(kind)
+
+
+@pytest.mark.parametrize("kind", ["all_padding", "one_expert", "last_expert_only", "ids_out_of_range",
+                                  "many_blocks", "no_split_k128"])
+def test_plain_call_edge_ids(gpu_device, kind):
+    ids, G, K = plain_ids_case(kind)
+    M, N = len(ids), 256
+    rng = np.random.Generator(np.random.PCG64(32))
+    a, sa_t = gen.quantize_lhs(gen.normal_with_outliers(rng, (M, K)))
+    sa_t = np.ascontiguousarray(sa_t.T)
+    b, sb = gen.make_grouped_rhs(G, N, K, 33)
+    d = sentinel_bf16((M, N))
+    ops.dg_fp8_grouped_gemm_contiguous(dev(a), dev(sa_t).t(), dev(b), dev(sb), dev(ids), d=d)
+    torch.cuda.synchronize()
+    got = bits(d)
+    # a block's expert is its largest id in [0, G); only rows with that id are written
+    blk = np.where((ids >= 0) & (ids < G), ids, -1).reshape(-1, 128).max(axis=1)
+    written = ids == np.repeat(blk, 128)
+    written &= ids >= 0
+    assert np.all(got[~written] == SENTINEL), kind
+    if not written.any():
+        return
+    rows = np.nonzero(written)[0]
+    if len(rows) > 4096:
+        rows = np.sort(rng.choice(rows, 4096, replace=False))
+    ns = np.tile(np.arange(0, N, 17), len(rows))
+    rr = np.repeat(rows, len(np.arange(0, N, 17)))
+    ref, _, produced = oracle.grouped_contiguous_points(a, sa_t.T, b, sb, ids, rr, ns)
+    assert produced.all()
+    assert_close(got[rr, ns], ref, "plain call edge case %s" % kind)
