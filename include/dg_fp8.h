@@ -162,7 +162,7 @@ int dg_fp8_gemm_nt_fmt(const void *A, int a_fmt, int64_t lda,
  * Layout contract: M_total % 128 == 0 and within every aligned 128-row block
  * all ids in [0, G) are equal (segments padded to 128). A block's expert is
  * the largest id in the block; a row whose id differs from it is not written.
- * Tiling: for e4m3 operands with N % 256 == 0, G <= 1024 and at most 4096
+ * Tiling: for e4m3 operands with N % 256 == 0, G <= 128 and at most 4096
  * blocks of 128 rows, a one-workgroup kernel first derives each expert's
  * segment offsets from expert_ids on the device, into a per-stream buffer of
  * (G + 2) int32 kept by the library (allocated like the split-K workspace of
