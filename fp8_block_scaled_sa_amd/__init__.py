@@ -8,6 +8,8 @@ contiguous layout. The kernels live in libdg_fp8.so behind
 the C ABI of include/dg_fp8.h; this package is its thin Python binding.
 """
 from .ops import (DGError, dg_fp8_gemm_nt, dg_fp8_gemm_nt_fmt, dg_fp8_grouped_gemm_contiguous,  # noqa: F401
+                  dg_fp8_gemm_nt_ws, dg_fp8_gemm_nt_workspace_bytes, dg_fp8_grouped_gemm_contiguous_ws,
+                  dg_fp8_grouped_gemm_contiguous_workspace_bytes, workspace,
                   dg_fp8_grouped_gemm_contiguous_fmt, dg_fp8_grouped_gemm_contiguous_layout,
                   dg_fp8_grouped_gemm_contiguous_to_tokens,
                   dg_fp8_grouped_gemm_masked_fmt,

@@ -16,6 +16,13 @@ SIGNATURES = {
     "dg_last_hip_error": (ctypes.c_int, []),
     "dg_fp8_gemm_nt": (ctypes.c_int, [_p, _i64, _p, _i64, _i64, _p, _i64, _p, _i64, _i64,
                                       _p, _i64, _i64, _i64, _i64, _p]),
+    "dg_fp8_gemm_nt_ws": (ctypes.c_int, [_p, _i64, _p, _i64, _i64, _p, _i64, _p, _i64, _i64,
+                                         _p, _i64, _i64, _i64, _i64, _p, _i64, _p]),
+    "dg_fp8_gemm_nt_workspace_bytes": (ctypes.c_int64, [_i64, _i64, _i64]),
+    "dg_fp8_grouped_gemm_contiguous_ws": (ctypes.c_int, [_p, _i64, _p, _i64, _i64, _p, _i64, _i64,
+                                                         _p, _i64, _i64, _i64, _p, _p, _p, _p, _i64, _i64,
+                                                         _i64, _i64, _i64, _i64, _p, _i64, _p]),
+    "dg_fp8_grouped_gemm_contiguous_workspace_bytes": (ctypes.c_int64, [_i64, _i64, _i64, _i64]),
     "dg_fp8_gemm_nt_fmt": (ctypes.c_int, [_p, ctypes.c_int, _i64, _p, _i64, _i64, _p, ctypes.c_int, _i64,
                                           _p, _i64, _i64, _p, _i64, _i64, _i64, _i64, _p]),
     "dg_fp8_grouped_gemm_contiguous": (ctypes.c_int, [_p, _i64, _p, _i64, _i64, _p, _i64, _i64,

@@ -8,6 +8,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 SOURCES = [os.path.join(HERE, "csrc", "dg_fp8.hip")]
 DEPS = SOURCES + [os.path.join(HERE, "csrc", "kernels.hpp"), os.path.join(HERE, "csrc", "quant.hpp"),
+        os.path.join(HERE, "csrc", "moe.hpp"),
         os.path.join(ROOT, "include", "dg_fp8.h")]
 LIBRARY = os.path.join(HERE, "libdg_fp8.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

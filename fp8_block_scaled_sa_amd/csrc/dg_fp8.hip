@@ -1,10 +1,13 @@
 // dg_fp8.hip -- C ABI of the gfx950 block-scaled FP8 GEMM (declared in
 // include/dg_fp8.h): host-side validation, device check, kernel choice and
-// launch. No device memory is allocated and no stream is synchronised.
+// launch. The library allocates no device memory and synchronises no stream:
+// the scratch memory some paths use (split-K partial sums, segment offsets
+// derived on the device) is the caller's workspace, passed to the *_ws entry
+// points; without one those paths run unsplit.
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
-#include <map>
+#include <initializer_list>
 #include <mutex>
 #include <stdlib.h>
 #include <stdint.h>
@@ -59,54 +62,37 @@ int current_device(DeviceInfo &out)
     return d.gfx950 ? DG_OK : DG_ERR_UNSUPPORTED;
 }
 
-// Split-K partial sums live in a device buffer per (device, stream), kept for
-// the life of the process and grown on demand. Calls on one stream run in
-// order, so they can share it; calls on different streams get their own.
-struct Workspace {
-    float *ptr = nullptr;
-    size_t bytes = 0;
-};
-using WorkspaceMap = std::map<std::pair<int, hipStream_t>, Workspace>;
-WorkspaceMap g_workspaces;
-WorkspaceMap g_aux;  // segment offsets derived on the device (a few KB per stream)
-std::mutex g_workspaces_mu;
+// One call's launch context: the device's CU count, the caller's stream and
+// the caller's workspace. The library owns no device memory: every step that
+// can use scratch (split-K partial sums, segment offsets derived on the
+// device) takes a region of the workspace the caller passed, or runs its path
+// without scratch when there is none or too little. A dry run launches
+// nothing and only records how many workspace bytes the fastest path would
+// take (what the *_workspace_bytes queries report).
+struct Ctx {
+    int cus = 0;
+    hipStream_t stream = nullptr;
+    uint8_t *ws = nullptr;  // caller's workspace (device), may be null
+    size_t ws_bytes = 0;
+    size_t need = 0;        // most workspace bytes any step asked for
+    bool dry = false;
 
-// A buffer of at least `bytes` for `stream`, or nullptr (allocation failed,
-// or the stream is being captured into a graph and has no large-enough
-// buffer yet: nothing is allocated or synchronised during a capture).
-// Growing waits for the stream, whose queued kernels may still use the old one.
-float *stream_buffer(WorkspaceMap &m, hipStream_t stream, size_t bytes)
-{
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess)
-        return nullptr;
-    std::lock_guard<std::mutex> lk(g_workspaces_mu);
-    Workspace &w = m[{dev, stream}];
-    if (w.bytes >= bytes)
-        return w.ptr;
-    hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
-    if (hipStreamIsCapturing(stream, &cs) != hipSuccess || cs != hipStreamCaptureStatusNone)
-        return nullptr;
-    if (w.ptr) {
-        if (hipStreamSynchronize(stream) != hipSuccess)
+    // Bytes of the workspace available from offset `off` on.
+    size_t avail(size_t off) const { return ws && ws_bytes > off ? ws_bytes - off : 0; }
+    // Records that a step would take `want` bytes at `off`; returns the region
+    // if the workspace holds it, else nullptr.
+    void *take(size_t off, size_t want)
+    {
+        need = std::max(need, off + want);
+        if (dry || want > avail(off))
             return nullptr;
-        (void)hipFree(w.ptr);
-        w.ptr = nullptr;
-        w.bytes = 0;
+        return ws + off;
     }
-    const size_t want = (bytes + (1u << 20) - 1) & ~(size_t)((1u << 20) - 1);
-    void *ptr = nullptr;
-    if (hipMalloc(&ptr, want) != hipSuccess) {
-        (void)hipGetLastError();  // clear the sticky error; the caller falls back to no split
-        return nullptr;
-    }
-    w.ptr = (float *)ptr;
-    w.bytes = want;
-    return w.ptr;
-}
+};
 
-float *stream_workspace(hipStream_t stream, size_t bytes) { return stream_buffer(g_workspaces, stream, bytes); }
-int32_t *stream_aux(hipStream_t stream, size_t bytes) { return (int32_t *)stream_buffer(g_aux, stream, bytes); }
+// Workspace regions start on 256-byte boundaries.
+constexpr size_t kWsAlign = 256;
+size_t ws_round(size_t b) { return (b + kWsAlign - 1) / kWsAlign * kWsAlign; }
 
 // Most experts for which the contiguous call given only ids derives segment offsets.
 constexpr int64_t kDeriveMaxExperts = 128;
@@ -180,7 +166,7 @@ int tile_override()
 }
 
 template <int L, class C, int F = 0, bool SCATTER = false>
-int launch_tiles(dgk::Params &p, int groups, int cus, hipStream_t stream)
+int launch_tiles(dgk::Params &p, int groups, Ctx &c)
 {
     if (p.N % C::kBN != 0)
         return DG_ERR_UNSUPPORTED;  // every config is chosen so that its BN divides N
@@ -190,25 +176,27 @@ int launch_tiles(dgk::Params &p, int groups, int cus, hipStream_t stream)
     if (tiles > kInt32Max)
         return DG_ERR_UNSUPPORTED;
     p.num_tiles = (int)tiles;
-    if (p.num_tiles == 0)
+    if (p.num_tiles == 0 || c.dry)
         return DG_OK;
-    const int grid = p.num_tiles < cus ? p.num_tiles : cus;  // persistent: one workgroup per CU
-    hipLaunchKernelGGL((dgk::tile_kernel<L, C, F, SCATTER>), dim3(grid), dim3(C::kThreads), 0, stream, p);
+    const int grid = p.num_tiles < c.cus ? p.num_tiles : c.cus;  // persistent: one workgroup per CU
+    hipLaunchKernelGGL((dgk::tile_kernel<L, C, F, SCATTER>), dim3(grid), dim3(C::kThreads), 0, c.stream, p);
     hipError_t e = hipGetLastError();
     return e == hipSuccess ? DG_OK : fail_hip(e);
 }
 
 // Contiguous layout on segment-aligned tiles (tile_kernel's SEG mode). The
 // real tile count depends on the device-side layout; each grid covers a bound
-// and the kernel skips the rest. With a workspace, the whole 256-row tiles run
-// first (they fill whole rounds when the segments are long), then the 128-row
-// tails split over K (their rows are few, but each would otherwise take about
-// as long as a whole tile), then a reduction adds the tails' slices in order.
+// and the kernel skips the rest. With workspace for it (from byte `ws_off`
+// on), the whole 256-row tiles run first (they fill whole rounds when the
+// segments are long), then the 128-row tails split over K (their rows are
+// few, but each would otherwise take about as long as a whole tile), then a
+// reduction adds the tails' slices in order. Without it the tails run
+// unsplit in the same launch as the whole tiles.
 template <class C, class CT, bool SCATTER>
-int launch_contiguous_seg(dgk::Params &p, int cus, hipStream_t stream)
+int launch_contiguous_seg(dgk::Params &p, Ctx &c, size_t ws_off)
 {
     static_assert(C::kBM == 256 && CT::kBM == 128, "whole tiles 256 rows, tails 128");
-    if (p.N % C::kBN != 0)
+    if (p.N % C::kBN != 0 || p.N % CT::kBN != 0)
         return DG_ERR_UNSUPPORTED;
     p.tiles_n = p.N / C::kBN;
     p.tiles_m = (p.M + 255) / 256 + p.G;
@@ -220,17 +208,25 @@ int launch_contiguous_seg(dgk::Params &p, int cus, hipStream_t stream)
     p.ksplit = 1;
     // At most this many K slices per tail, at least four K blocks each; the
     // kernels pick the count from the number of tails they find. No split
-    // when the tails alone would fill two rounds of the CUs.
-    if (p.N % CT::kBN != 0)
-        return DG_ERR_UNSUPPORTED;
+    // when the tails alone would fill two rounds of the CUs. A workspace too
+    // small for every slice takes as many slices as it holds.
     const int64_t tail_tiles = (int64_t)p.G * (p.N / CT::kBN);
-    const int ks = tail_tiles >= 2 * (int64_t)cus || tile_override() == 23 ? 1 : std::min(dgk::kMaxTailSplit, (p.K / 128) / 4);
-    const size_t ws_bytes = (size_t)ks * p.G * 128 * p.N * sizeof(float);
-    float *ws = (ks >= 2 && ws_bytes <= ((size_t)1 << 30)) ? stream_workspace(stream, ws_bytes) : nullptr;
+    int ks = tail_tiles >= 2 * (int64_t)c.cus || tile_override() == 23 ? 1 : std::min(dgk::kMaxTailSplit, (p.K / 128) / 4);
+    const size_t slice_bytes = (size_t)p.G * 128 * p.N * sizeof(float);
+    float *ws = nullptr;
+    if (ks >= 2) {
+        ws = (float *)c.take(ws_off, ks * slice_bytes);
+        if (!ws && !c.dry) {
+            ks = (int)std::min<size_t>(ks, c.avail(ws_off) / slice_bytes);
+            ws = ks >= 2 ? (float *)(c.ws + ws_off) : nullptr;
+        }
+    }
+    if (c.dry)
+        return DG_OK;
     if (ws)
         p.seg_mode = 1;
     hipLaunchKernelGGL((dgk::tile_kernel<dgk::kContiguous, C, 0, SCATTER, true>),
-                       dim3(p.num_tiles < cus ? p.num_tiles : cus), dim3(C::kThreads), 0, stream, p);
+                       dim3(p.num_tiles < c.cus ? p.num_tiles : c.cus), dim3(C::kThreads), 0, c.stream, p);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess)
         return fail_hip(e);
@@ -243,12 +239,12 @@ int launch_contiguous_seg(dgk::Params &p, int cus, hipStream_t stream)
     q.ws_rows = p.G * 128;
     q.tiles_n = p.N / CT::kBN;
     q.num_tiles = p.G * q.tiles_n * ks;
-    q.tail_slots = q.num_tiles < cus ? q.num_tiles : cus;
+    q.tail_slots = q.num_tiles < c.cus ? q.num_tiles : c.cus;
     hipLaunchKernelGGL((dgk::tile_kernel<dgk::kContiguous, CT, 0, SCATTER, true>), dim3(q.tail_slots),
-                       dim3(CT::kThreads), 0, stream, q);
+                       dim3(CT::kThreads), 0, c.stream, q);
     if ((e = hipGetLastError()) != hipSuccess)
         return fail_hip(e);
-    hipLaunchKernelGGL(dgk::seg_tail_reduce_kernel, dim3(128, (unsigned)p.G), dim3(256), 0, stream, q);
+    hipLaunchKernelGGL(dgk::seg_tail_reduce_kernel, dim3(128, (unsigned)p.G), dim3(256), 0, c.stream, q);
     e = hipGetLastError();
     return e == hipSuccess ? DG_OK : fail_hip(e);
 }
@@ -256,13 +252,13 @@ int launch_contiguous_seg(dgk::Params &p, int cus, hipStream_t stream)
 // launch_tiles with the operand formats chosen at run time (bit 0: A is e5m2,
 // bit 1: B is e5m2); the formats only set the MFMA's format selectors.
 template <int L, class C>
-int launch_tiles_fmt(dgk::Params &p, int groups, int cus, hipStream_t stream, int f)
+int launch_tiles_fmt(dgk::Params &p, int groups, Ctx &c, int f)
 {
     switch (f) {
-    case 1: return launch_tiles<L, C, 1>(p, groups, cus, stream);
-    case 2: return launch_tiles<L, C, 2>(p, groups, cus, stream);
-    case 3: return launch_tiles<L, C, 3>(p, groups, cus, stream);
-    default: return launch_tiles<L, C, 0>(p, groups, cus, stream);
+    case 1: return launch_tiles<L, C, 1>(p, groups, c);
+    case 2: return launch_tiles<L, C, 2>(p, groups, c);
+    case 3: return launch_tiles<L, C, 3>(p, groups, c);
+    default: return launch_tiles<L, C, 0>(p, groups, c);
     }
 }
 
@@ -278,26 +274,32 @@ int format_bits(int a_fmt, int b_fmt)
 // (tiles * ks <= CUs, one round) that write fp32 partials; a second kernel
 // adds the slices in order and writes D.
 template <class C, int F = 0>
-int launch_dense(dgk::Params &p, int cus, hipStream_t stream)
+int launch_dense(dgk::Params &p, Ctx &c)
 {
     if (p.N % C::kBN != 0)
         return DG_ERR_UNSUPPORTED;
     const int64_t tiles = (int64_t)((p.M + C::kBM - 1) / C::kBM) * (p.N / C::kBN);
     const int nk = p.K / 128;
     int ks = 1;
-    if (tile_override() != 16 && tiles * 2 <= cus && nk >= 2)
-        ks = (int)std::min<int64_t>(std::min<int64_t>(nk, cus / tiles), 8);
+    if (tile_override() != 16 && tiles * 2 <= c.cus && nk >= 2)
+        ks = (int)std::min<int64_t>(std::min<int64_t>(nk, c.cus / tiles), 8);
     if (ks > 1) {
-        p.ws = stream_workspace(stream, (size_t)ks * p.M * p.N * sizeof(float));
+        // A workspace too small for every slice takes as many as it holds.
+        const size_t slice_bytes = (size_t)p.M * p.N * sizeof(float);
+        p.ws = (float *)c.take(0, ks * slice_bytes);
+        if (!p.ws && !c.dry) {
+            ks = (int)std::min<size_t>(ks, c.avail(0) / slice_bytes);
+            p.ws = ks >= 2 ? (float *)c.ws : nullptr;
+        }
         if (!p.ws)
             ks = 1;
     }
     p.ksplit = ks;
-    int st = launch_tiles<dgk::kDense, C, F>(p, ks, cus, stream);
-    if (st != DG_OK || ks == 1)
+    int st = launch_tiles<dgk::kDense, C, F>(p, ks, c);
+    if (st != DG_OK || ks == 1 || c.dry)
         return st;
     const int64_t quads = (int64_t)p.M * (p.N / 4);
-    hipLaunchKernelGGL(dgk::splitk_reduce_kernel, dim3((unsigned)((quads + 255) / 256)), dim3(256), 0, stream,
+    hipLaunchKernelGGL(dgk::splitk_reduce_kernel, dim3((unsigned)((quads + 255) / 256)), dim3(256), 0, c.stream,
                        p.ws, ks, p.M, p.N, p.D, p.ldd);
     hipError_t e = hipGetLastError();
     return e == hipSuccess ? DG_OK : fail_hip(e);
@@ -337,14 +339,14 @@ TileCut round_cut(int64_t tiles_m, int64_t tiles_n, int cus)
 // fill the CUs (a last round at most half full is cut off and run with
 // smaller tiles); below that, smaller tiles split over K.
 template <int F = 0>
-int launch_dense_auto(dgk::Params &p, int cus, hipStream_t s)
+int launch_dense_auto(dgk::Params &p, Ctx &cx)
 {
     const bool wide_n = p.N % 256 == 0;
     const int64_t tiles_m = (p.M + 255) / 256, tiles_n = p.N / 256;
-    if (wide_n && tiles_m * tiles_n * 2 > cus) {
-        const TileCut c = round_cut(tiles_m, tiles_n, cus);
+    if (wide_n && tiles_m * tiles_n * 2 > cx.cus) {
+        const TileCut c = round_cut(tiles_m, tiles_n, cx.cus);
         if (c.cut_n == 0 && c.cut_m == 0)
-            return launch_dense<CfgBig, F>(p, cus, s);
+            return launch_dense<CfgBig, F>(p, cx);
         dgk::Params main = p, rest = p;
         if (c.cut_n) {  // columns [0, N1) whole rounds; the rest on 256x128 tiles
             const int64_t N1 = 256 * c.cut_n;
@@ -361,14 +363,15 @@ int launch_dense_auto(dgk::Params &p, int cus, hipStream_t s)
             rest.D += M1 * p.ldd;
             rest.M = p.M - (int)M1;
         }
-        const int st = launch_dense<CfgBig, F>(main, cus, s);
+        // the two launches run in stream order, so the strip may reuse the workspace
+        const int st = launch_dense<CfgBig, F>(main, cx);
         if (st != DG_OK)
             return st;
-        return c.cut_n ? launch_dense<CfgDense, F>(rest, cus, s) : launch_dense_auto<F>(rest, cus, s);
+        return c.cut_n ? launch_dense<CfgDense, F>(rest, cx) : launch_dense_auto<F>(rest, cx);
     }
     if (p.M <= 128)
-        return launch_dense<CfgNarrow, F>(p, cus, s);
-    return launch_dense<CfgDense, F>(p, cus, s);
+        return launch_dense<CfgNarrow, F>(p, cx);
+    return launch_dense<CfgDense, F>(p, cx);
 }
 
 // Per-lane DMA offsets are 32-bit: a tile's rows of A, B and sA must span < 2^32 bytes.
@@ -386,8 +389,9 @@ constexpr int decode_dma_lds(int nb, int mr)
 // decode_dma_kernel for NB K blocks per wave and MR staged LHS rows; false if
 // that instantiation does not fit the LDS.
 template <int MR, int MP = 1>
-bool launch_decode_dma(const dgk::Params &p, int nb, bool full, hipStream_t stream)
+bool launch_decode_dma(const dgk::Params &p, int nb, bool full, const Ctx &c)
 {
+    hipStream_t stream = c.stream;
     const dim3 g(p.N / 16), b(dgk::kDecodeThreads);
     bool done = false;
     auto one = [&](auto nb_c) {
@@ -397,13 +401,15 @@ bool launch_decode_dma(const dgk::Params &p, int nb, bool full, hipStream_t stre
         if constexpr (decode_dma_lds(NB, MR) <= 160 * 1024 && MP * 1024 <= NB * MR * 128 && (MP == 1 || NB <= 8)) {
             if (nb != NB)
                 return;
+            done = true;
+            if (c.dry)
+                return;
             if (full && (p.ldb & 4095) == 0)   // rotated block order (see the kernel)
                 hipLaunchKernelGGL((dgk::decode_dma_kernel<NB, MR, true, MP, true>), g, b, 0, stream, p);
             else if (full)
                 hipLaunchKernelGGL((dgk::decode_dma_kernel<NB, MR, true, MP>), g, b, 0, stream, p);
             else
                 hipLaunchKernelGGL((dgk::decode_dma_kernel<NB, MR, false, MP>), g, b, 0, stream, p);
-            done = true;
         }
     };
     one(std::integral_constant<int, 1>{});
@@ -430,8 +436,9 @@ constexpr int kDecodeDeclined = -1;
 // Small-M kernels. The LHS-staging kernel (up to 4 passes of 16 rows) is
 // tried first; when its LDS does not fit the shape, the older decode kernels
 // run if `fallback` (M <= 24 or short K), else kDecodeDeclined.
-int launch_decode(dgk::Params &p, hipStream_t stream, bool fallback)
+int launch_decode(dgk::Params &p, const Ctx &c, bool fallback)
 {
+    hipStream_t stream = c.stream;
     const int grid = p.N / 16;
     hipError_t e;
     const int64_t nkb = p.K / 128;
@@ -441,13 +448,15 @@ int launch_decode(dgk::Params &p, hipStream_t stream, bool fallback)
                         ((int64_t)(p.M - 1) * p.sa_m + (nkb - 1) * p.sa_kb) * 4 < ((int64_t)1 << 31);
     const int nb = (int)(nkb / dgk::kDecodeWaves);
     const bool full = tile_override() != 6;
-    if (dma_ok && p.M <= 8 && launch_decode_dma<8>(p, nb, full, stream)) {
-    } else if (dma_ok && p.M <= 16 && launch_decode_dma<16>(p, nb, full, stream)) {
-    } else if (dma_ok && p.M <= 32 && launch_decode_dma<16, 2>(p, nb, full, stream)) {
-    } else if (dma_ok && p.M <= 48 && launch_decode_dma<16, 3>(p, nb, full, stream)) {
-    } else if (dma_ok && p.M <= 64 && launch_decode_dma<16, 4>(p, nb, full, stream)) {
+    if (dma_ok && p.M <= 8 && launch_decode_dma<8>(p, nb, full, c)) {
+    } else if (dma_ok && p.M <= 16 && launch_decode_dma<16>(p, nb, full, c)) {
+    } else if (dma_ok && p.M <= 32 && launch_decode_dma<16, 2>(p, nb, full, c)) {
+    } else if (dma_ok && p.M <= 48 && launch_decode_dma<16, 3>(p, nb, full, c)) {
+    } else if (dma_ok && p.M <= 64 && launch_decode_dma<16, 4>(p, nb, full, c)) {
     } else if (!fallback) {
         return kDecodeDeclined;
+    } else if (c.dry) {
+        return DG_OK;   // one of the older decode kernels below; they take no workspace
     } else if (p.M <= 16 && nkb % dgk::kDecodeWaves == 0 && nkb / dgk::kDecodeWaves <= 8 && tile_override() != 7 &&
         tile_override() != 8) {
         const dim3 g(grid), b(dgk::kDecodeThreads);
@@ -471,6 +480,8 @@ int launch_decode(dgk::Params &p, hipStream_t stream, bool fallback)
         hipLaunchKernelGGL(dgk::decode_kernel<2>, dim3(grid), dim3(dgk::kDecodeThreads), 0, stream, p);
     else
         hipLaunchKernelGGL(dgk::decode_kernel<4>, dim3(grid), dim3(dgk::kDecodeThreads), 0, stream, p);
+    if (c.dry)
+        return DG_OK;
     e = hipGetLastError();
     return e == hipSuccess ? DG_OK : fail_hip(e);
 }
@@ -544,14 +555,34 @@ int quantize_impl(const void *X, int x_dtype, int64_t ldx, int64_t x_rows, const
     return e == hipSuccess ? DG_OK : fail_hip(e);
 }
 
+// A caller workspace must be 16-byte aligned, have a non-negative size and
+// lie apart from the call's output and inputs.
+int check_workspace(const void *ws, int64_t ws_bytes, std::initializer_list<Extent> others)
+{
+    if (ws_bytes < 0)
+        return DG_ERR_BAD_SHAPE;
+    if (!ws || ws_bytes == 0)
+        return DG_OK;
+    if (!aligned(ws, 16))
+        return DG_ERR_MISALIGNED;
+    const Extent ew = extent(ws, 1, ws_bytes - 1);
+    for (const Extent &e : others)
+        if (e.hi > e.lo && overlaps(ew, e))
+            return DG_ERR_ALIASING;
+    return DG_OK;
+}
+
 // Validation and kernel arguments of a dense call. Returns DG_OK with `p`
 // and `dev` filled, kEmptyProblem for an empty problem, or an error.
 constexpr int kEmptyProblem = -2;
 
 int dense_setup(const void *A, int64_t lda, const float *sA, int64_t sa_stride_m, int64_t sa_stride_kb,
                 const void *B, int64_t ldb, const float *sB, int64_t sb_stride_nb, int64_t sb_stride_kb,
-                void *D, int64_t ldd, int64_t M, int64_t N, int64_t K, dgk::Params &p, DeviceInfo &dev)
+                void *D, int64_t ldd, int64_t M, int64_t N, int64_t K, dgk::Params &p, DeviceInfo &dev,
+                const void *workspace = nullptr, int64_t ws_bytes = 0)
 {
+    if (ws_bytes < 0)
+        return DG_ERR_BAD_SHAPE;
     int st = check_common_shape(M, N, K);
     if (st != DG_OK)
         return st;
@@ -567,10 +598,13 @@ int dense_setup(const void *A, int64_t lda, const float *sA, int64_t sa_stride_m
         return DG_ERR_MISALIGNED;
     const int64_t nkb = K / 128;
     const Extent ed = extent(D, 2, (M - 1) * ldd + N - 1);
-    if (overlaps(ed, extent(A, 1, (M - 1) * lda + K - 1)) || overlaps(ed, extent(B, 1, (N - 1) * ldb + K - 1)) ||
-        overlaps(ed, extent(sA, 4, last_scale_index(M, nkb, sa_stride_m, sa_stride_kb))) ||
-        overlaps(ed, extent(sB, 4, last_scale_index(N / 128, nkb, sb_stride_nb, sb_stride_kb))))
+    const Extent ea = extent(A, 1, (M - 1) * lda + K - 1), eb = extent(B, 1, (N - 1) * ldb + K - 1);
+    const Extent esa = extent(sA, 4, last_scale_index(M, nkb, sa_stride_m, sa_stride_kb));
+    const Extent esb = extent(sB, 4, last_scale_index(N / 128, nkb, sb_stride_nb, sb_stride_kb));
+    if (overlaps(ed, ea) || overlaps(ed, eb) || overlaps(ed, esa) || overlaps(ed, esb))
         return DG_ERR_ALIASING;
+    if ((st = check_workspace(workspace, ws_bytes, {ed, ea, eb, esa, esb})) != DG_OK)
+        return st;
     if ((st = current_device(dev)) != DG_OK)
         return st;
 
@@ -584,14 +618,85 @@ int dense_setup(const void *A, int64_t lda, const float *sA, int64_t sa_stride_m
     return DG_OK;
 }
 
+// Kernel choice and launches of the contiguous grouped GEMM (arguments
+// already validated; in a dry run only the workspace need is recorded).
+// scatter: rows go to token order (p.row_dst); fmt as for launch_tiles_fmt.
+int contiguous_dispatch(dgk::Params &p, Ctx &c, bool scatter, int fmt)
+{
+    const int64_t N = p.N, G = p.G;
+    int st = DG_OK;
+    if (p.layout) {
+        const bool wide = N % 256 == 0;
+        if (scatter)
+            return wide ? launch_contiguous_seg<CfgBig, CfgTail, true>(p, c, 0)
+                        : launch_contiguous_seg<CfgDense, CfgNarrow, true>(p, c, 0);
+        return wide ? launch_contiguous_seg<CfgBig, CfgTail, false>(p, c, 0)
+                    : launch_contiguous_seg<CfgDense, CfgNarrow, false>(p, c, 0);
+    }
+    // Only the ids given: with workspace for the offsets, derive the segment
+    // offsets on the device and tile along them (e4m3, 256-wide tiles, at
+    // most 4096 blocks of 128 rows). The uniform-grid launch below then runs
+    // only if the ids' experts were not in ascending order, which the
+    // derivation flags. Up to 128 experts: at 8192 tokens, N 4096, K 7168 this
+    // measured 9-31% faster than the uniform grid for 8-64 experts and 2%
+    // faster at 128; at 256 (every segment one 128-row block) it was 2%
+    // slower, the per-tile segment search then outweighing the saved
+    // two-expert passes. Workspace: the offsets first (G + 2 int32), then the
+    // split tails' partial sums.
+    const int ov = tile_override();  // 24: no derivation; 2, 3, 4 force the uniform grid's tile shape
+    if (!fmt && N % 256 == 0 && G <= kDeriveMaxExperts && p.M / 128 <= dgm::kDeriveMaxBlocks && ov != 24 &&
+        ov != 2 && ov != 3 && ov != 4) {
+        const size_t aux_bytes = ws_round((size_t)(G + 2) * sizeof(int32_t));
+        int32_t *aux = (int32_t *)c.take(0, aux_bytes);
+        if (aux || c.dry) {
+            if (!c.dry) {
+                dgm::DeriveParams dp = {p.ids, p.M, p.G, aux, aux + G + 1};
+                hipLaunchKernelGGL(dgm::derive_layout_kernel, dim3(1), dim3(dgm::kRouteThreads), 0, c.stream, dp);
+                const hipError_t e = hipGetLastError();
+                if (e != hipSuccess)
+                    return fail_hip(e);
+            }
+            dgk::Params q = p;
+            q.layout = aux;
+            st = scatter ? launch_contiguous_seg<CfgBig, CfgTail, true>(q, c, aux_bytes)
+                         : launch_contiguous_seg<CfgBig, CfgTail, false>(q, c, aux_bytes);
+            if (st != DG_OK)
+                return st;
+            if (aux)
+                p.gate = aux + G + 1;
+        }
+    }
+    if (scatter) {
+        if (N % 256 == 0)
+            return launch_tiles<dgk::kContiguous, CfgBig, 0, true>(p, 1, c);
+        return launch_tiles<dgk::kContiguous, CfgDense, 0, true>(p, 1, c);
+    }
+    if (fmt) {
+        if (N % 256 == 0)
+            return launch_tiles_fmt<dgk::kContiguous, CfgBig>(p, 1, c, fmt);
+        return launch_tiles_fmt<dgk::kContiguous, CfgDense>(p, 1, c, fmt);
+    }
+    switch (ov) {
+    case 2: return launch_tiles<dgk::kContiguous, CfgNarrow>(p, 1, c);
+    case 3: return launch_tiles<dgk::kContiguous, CfgWide>(p, 1, c);
+    case 4: return launch_tiles<dgk::kContiguous, CfgDense>(p, 1, c);
+    default:
+        if (N % 256 == 0)
+            return launch_tiles<dgk::kContiguous, CfgBig>(p, 1, c);
+        return launch_tiles<dgk::kContiguous, CfgDense>(p, 1, c);
+    }
+}
+
 // The contiguous grouped GEMM. With token_of_row, row r of the result is
 // written to row token_of_row[r] of D (D has d_rows rows); without it, to row r
-// (d_rows = M_total).
+// (d_rows = M_total). workspace / ws_bytes: the caller's scratch memory (may
+// be null / 0).
 int contiguous_impl(const void *A, int64_t lda, const float *sA, int64_t sa_stride_m, int64_t sa_stride_kb,
                     const void *B, int64_t ldb, int64_t b_stride_g, const float *sB, int64_t sb_stride_g,
                     int64_t sb_stride_nb, int64_t sb_stride_kb, const int32_t *expert_ids,
                     const int32_t *token_of_row, void *D, int64_t ldd, int64_t d_rows, int64_t M_total, int64_t N,
-                    int64_t K, int64_t G, void *stream, int fmt = 0, const int32_t *layout = nullptr)
+                    int64_t K, int64_t G, void *stream, int fmt = 0, const int32_t *layout = nullptr,
+                    void *workspace = nullptr, int64_t ws_bytes = 0)
 {
     int st = check_common_shape(M_total, N, K);
     if (st != DG_OK)
@@ -600,7 +705,7 @@ int contiguous_impl(const void *A, int64_t lda, const float *sA, int64_t sa_stri
         return DG_ERR_BAD_SHAPE;
     if (G > kInt32Max)
         return DG_ERR_UNSUPPORTED;
-    if (d_rows < 0)
+    if (d_rows < 0 || ws_bytes < 0)
         return DG_ERR_BAD_SHAPE;
     if (d_rows > kInt32Max)
         return DG_ERR_UNSUPPORTED;
@@ -623,12 +728,19 @@ int contiguous_impl(const void *A, int64_t lda, const float *sA, int64_t sa_stri
     if ((token_of_row && overlaps(ed, extent(token_of_row, 4, M_total - 1))) ||
         (layout && overlaps(ed, extent(layout, 4, G))))
         return DG_ERR_ALIASING;
-    if (overlaps(ed, extent(A, 1, (M_total - 1) * lda + K - 1)) ||
-        overlaps(ed, extent(B, 1, (G - 1) * b_stride_g + (N - 1) * ldb + K - 1)) ||
-        overlaps(ed, extent(sA, 4, last_scale_index(M_total, nkb, sa_stride_m, sa_stride_kb))) ||
-        overlaps(ed, extent(sB, 4, (G - 1) * sb_stride_g + last_scale_index(N / 128, nkb, sb_stride_nb, sb_stride_kb))) ||
-        overlaps(ed, extent(expert_ids, 4, M_total - 1)))
+    const Extent ea = extent(A, 1, (M_total - 1) * lda + K - 1);
+    const Extent eb = extent(B, 1, (G - 1) * b_stride_g + (N - 1) * ldb + K - 1);
+    const Extent esa = extent(sA, 4, last_scale_index(M_total, nkb, sa_stride_m, sa_stride_kb));
+    const Extent esb = extent(sB, 4, (G - 1) * sb_stride_g + last_scale_index(N / 128, nkb, sb_stride_nb, sb_stride_kb));
+    const Extent eid = extent(expert_ids, 4, M_total - 1);
+    if (overlaps(ed, ea) || overlaps(ed, eb) || overlaps(ed, esa) || overlaps(ed, esb) || overlaps(ed, eid))
         return DG_ERR_ALIASING;
+    const Extent none{0, 0};
+    st = check_workspace(workspace, ws_bytes,
+                         {ed, ea, eb, esa, esb, eid, token_of_row ? extent(token_of_row, 4, M_total - 1) : none,
+                          layout ? extent(layout, 4, G) : none});
+    if (st != DG_OK)
+        return st;
     DeviceInfo dev;
     if ((st = current_device(dev)) != DG_OK)
         return st;
@@ -645,62 +757,12 @@ int contiguous_impl(const void *A, int64_t lda, const float *sA, int64_t sa_stri
     p.M = (int)M_total; p.N = (int)N; p.K = (int)K; p.G = (int)G;
     if (!offsets_fit(lda, ldb, sa_stride_m))
         return DG_ERR_UNSUPPORTED;
-    if (layout) {
-        const bool wide = N % 256 == 0;
-        if (token_of_row)
-            return wide ? launch_contiguous_seg<CfgBig, CfgTail, true>(p, dev.cus, (hipStream_t)stream)
-                        : launch_contiguous_seg<CfgDense, CfgNarrow, true>(p, dev.cus, (hipStream_t)stream);
-        return wide ? launch_contiguous_seg<CfgBig, CfgTail, false>(p, dev.cus, (hipStream_t)stream)
-                    : launch_contiguous_seg<CfgDense, CfgNarrow, false>(p, dev.cus, (hipStream_t)stream);
-    }
-    // Only the ids given: derive the segment offsets on the device and tile
-    // along them (e4m3, 256-wide tiles, at most 4096 blocks of 128 rows,
-    // outside graph capture unless the stream's buffer exists). The
-    // uniform-grid launch below then runs only if the ids' experts were not
-    // in ascending order, which the derivation flags. Up to 128 experts: at
-    // 8192 tokens, N 4096, K 7168 this measured 9-31% faster than the uniform
-    // grid for 8-64 experts and 2% faster at 128; at 256 (every segment one
-    // 128-row block) it was 2% slower, the per-tile segment search then
-    // outweighing the saved two-expert passes.
-    const int ov = tile_override();  // 24: no derivation; 2, 3, 4 force the uniform grid's tile shape
-    if (!fmt && N % 256 == 0 && G <= kDeriveMaxExperts && M_total / 128 <= dgm::kDeriveMaxBlocks && ov != 24 &&
-        ov != 2 && ov != 3 && ov != 4) {
-        int32_t *aux = stream_aux((hipStream_t)stream, (size_t)(G + 2) * sizeof(int32_t));
-        if (aux) {
-            dgm::DeriveParams dp = {expert_ids, (int)M_total, (int)G, aux, aux + G + 1};
-            hipLaunchKernelGGL(dgm::derive_layout_kernel, dim3(1), dim3(dgm::kRouteThreads), 0, (hipStream_t)stream,
-                               dp);
-            const hipError_t e = hipGetLastError();
-            if (e != hipSuccess)
-                return fail_hip(e);
-            dgk::Params q = p;
-            q.layout = aux;
-            st = token_of_row ? launch_contiguous_seg<CfgBig, CfgTail, true>(q, dev.cus, (hipStream_t)stream)
-                              : launch_contiguous_seg<CfgBig, CfgTail, false>(q, dev.cus, (hipStream_t)stream);
-            if (st != DG_OK)
-                return st;
-            p.gate = aux + G + 1;
-        }
-    }
-    if (token_of_row) {
-        if (N % 256 == 0)
-            return launch_tiles<dgk::kContiguous, CfgBig, 0, true>(p, 1, dev.cus, (hipStream_t)stream);
-        return launch_tiles<dgk::kContiguous, CfgDense, 0, true>(p, 1, dev.cus, (hipStream_t)stream);
-    }
-    if (fmt) {
-        if (N % 256 == 0)
-            return launch_tiles_fmt<dgk::kContiguous, CfgBig>(p, 1, dev.cus, (hipStream_t)stream, fmt);
-        return launch_tiles_fmt<dgk::kContiguous, CfgDense>(p, 1, dev.cus, (hipStream_t)stream, fmt);
-    }
-    switch (tile_override()) {
-    case 2: return launch_tiles<dgk::kContiguous, CfgNarrow>(p, 1, dev.cus, (hipStream_t)stream);
-    case 3: return launch_tiles<dgk::kContiguous, CfgWide>(p, 1, dev.cus, (hipStream_t)stream);
-    case 4: return launch_tiles<dgk::kContiguous, CfgDense>(p, 1, dev.cus, (hipStream_t)stream);
-    default:
-        if (N % 256 == 0)
-            return launch_tiles<dgk::kContiguous, CfgBig>(p, 1, dev.cus, (hipStream_t)stream);
-        return launch_tiles<dgk::kContiguous, CfgDense>(p, 1, dev.cus, (hipStream_t)stream);
-    }
+    Ctx c;
+    c.cus = dev.cus;
+    c.stream = (hipStream_t)stream;
+    c.ws = (uint8_t *)workspace;
+    c.ws_bytes = workspace ? (size_t)ws_bytes : 0;
+    return contiguous_dispatch(p, c, token_of_row != nullptr, fmt);
 }
 
 // The masked grouped GEMM; fmt as for launch_tiles_fmt.
@@ -752,21 +814,55 @@ int masked_impl(const void *A, int64_t lda, int64_t a_stride_g, const float *sA,
     p.M = (int)M_max; p.N = (int)N; p.K = (int)K; p.G = (int)G;
     if (!offsets_fit(lda, ldb, sa_stride_m))
         return DG_ERR_UNSUPPORTED;
+    Ctx c;
+    c.cus = dev.cus;
+    c.stream = (hipStream_t)stream;
     if (fmt) {
         if (N % 256 == 0)
-            return launch_tiles_fmt<dgk::kMasked, CfgBigStreamB>(p, (int)G, dev.cus, (hipStream_t)stream, fmt);
-        return launch_tiles_fmt<dgk::kMasked, CfgDense>(p, (int)G, dev.cus, (hipStream_t)stream, fmt);
+            return launch_tiles_fmt<dgk::kMasked, CfgBigStreamB>(p, (int)G, c, fmt);
+        return launch_tiles_fmt<dgk::kMasked, CfgDense>(p, (int)G, c, fmt);
     }
     switch (tile_override()) {
-    case 1: return launch_tiles<dgk::kMasked, CfgDense4>(p, (int)G, dev.cus, (hipStream_t)stream);
-    case 2: return launch_tiles<dgk::kMasked, CfgNarrow>(p, (int)G, dev.cus, (hipStream_t)stream);
-    case 4: return launch_tiles<dgk::kMasked, CfgDense>(p, (int)G, dev.cus, (hipStream_t)stream);
-    case 12: return N % 256 == 0 ? launch_tiles<dgk::kMasked, CfgBig>(p, (int)G, dev.cus, (hipStream_t)stream)
+    case 1: return launch_tiles<dgk::kMasked, CfgDense4>(p, (int)G, c);
+    case 2: return launch_tiles<dgk::kMasked, CfgNarrow>(p, (int)G, c);
+    case 4: return launch_tiles<dgk::kMasked, CfgDense>(p, (int)G, c);
+    case 12: return N % 256 == 0 ? launch_tiles<dgk::kMasked, CfgBig>(p, (int)G, c)
                                  : DG_ERR_UNSUPPORTED;
     default:
         if (N % 256 == 0)
-            return launch_tiles<dgk::kMasked, CfgBigStreamB>(p, (int)G, dev.cus, (hipStream_t)stream);
-        return launch_tiles<dgk::kMasked, CfgDense>(p, (int)G, dev.cus, (hipStream_t)stream);
+            return launch_tiles<dgk::kMasked, CfgBigStreamB>(p, (int)G, c);
+        return launch_tiles<dgk::kMasked, CfgDense>(p, (int)G, c);
+    }
+}
+
+// Kernel choice and launches of the dense e4m3 GEMM (arguments validated;
+// in a dry run only the workspace need is recorded).
+int dense_dispatch(dgk::Params &p, Ctx &c)
+{
+    const int64_t M = p.M, nkb = p.K / 128;
+    // M <= 64: the decode kernels (B streamed once per launch, the LHS staged
+    // per wave 16 rows at a time). Where their LDS staging does not fit the
+    // shape, the older decode kernels keep M <= 24 and short K (< 16 blocks:
+    // a split-K launch pair costs more than it saves); the rest, and all
+    // larger M, go to the tile kernel, split over K when its tiles are few
+    // and the workspace holds the partial sums.
+    const bool forced_tiles = tile_override() == 1 || tile_override() == 2 || tile_override() == 4;
+    const int64_t decode_max_m = tile_override() == 13 ? 16 : 64;
+    if (M <= decode_max_m && !forced_tiles) {
+        const int st = launch_decode(p, c, M <= 24 || nkb < 16 || tile_override() == 14);
+        if (st != kDecodeDeclined)
+            return st;
+    }
+    if (!offsets_fit(p.lda, p.ldb, p.sa_m))
+        return DG_ERR_UNSUPPORTED;
+    const bool wide_n = p.N % 256 == 0;
+    switch (tile_override()) {
+    case 1: return launch_tiles<dgk::kDense, CfgDense4>(p, 1, c);
+    case 2: return launch_tiles<dgk::kDense, CfgNarrow>(p, 1, c);
+    case 4: return launch_tiles<dgk::kDense, CfgDense>(p, 1, c);
+    case 15: return wide_n ? launch_dense<CfgBig>(p, c) : launch_dense<CfgDense>(p, c);
+    default:
+        return launch_dense_auto(p, c);
     }
 }
 
@@ -776,7 +872,7 @@ extern "C" {
 
 int dg_abi_version(void) { return DG_ABI_VERSION; }
 
-const char *dg_status_string(int status)
+const char *dg_status_string(dg_status status)
 {
     switch (status) {
     case DG_OK: return "ok";
@@ -793,55 +889,66 @@ const char *dg_status_string(int status)
 
 int dg_last_hip_error(void) { return g_last_hip_error; }
 
-int dg_fp8_gemm_nt(const void *A, int64_t lda, const float *sA, int64_t sa_stride_m, int64_t sa_stride_kb,
-                   const void *B, int64_t ldb, const float *sB, int64_t sb_stride_nb, int64_t sb_stride_kb,
-                   void *D, int64_t ldd, int64_t M, int64_t N, int64_t K, void *stream)
+dg_status dg_fp8_gemm_nt(const void *A, int64_t lda, const float *sA, int64_t sa_stride_m, int64_t sa_stride_kb,
+                         const void *B, int64_t ldb, const float *sB, int64_t sb_stride_nb, int64_t sb_stride_kb,
+                         void *D, int64_t ldd, int64_t M, int64_t N, int64_t K, void *stream)
+{
+    return dg_fp8_gemm_nt_ws(A, lda, sA, sa_stride_m, sa_stride_kb, B, ldb, sB, sb_stride_nb, sb_stride_kb, D, ldd,
+                             M, N, K, nullptr, 0, stream);
+}
+
+dg_status dg_fp8_gemm_nt_ws(const void *A, int64_t lda, const float *sA, int64_t sa_stride_m, int64_t sa_stride_kb,
+                            const void *B, int64_t ldb, const float *sB, int64_t sb_stride_nb, int64_t sb_stride_kb,
+                            void *D, int64_t ldd, int64_t M, int64_t N, int64_t K, void *workspace,
+                            int64_t workspace_bytes, void *stream)
 {
     dgk::Params p;
     DeviceInfo dev;
     int st = dense_setup(A, lda, sA, sa_stride_m, sa_stride_kb, B, ldb, sB, sb_stride_nb, sb_stride_kb, D, ldd,
-                         M, N, K, p, dev);
+                         M, N, K, p, dev, workspace, workspace_bytes);
     if (st != DG_OK)
-        return st == kEmptyProblem ? DG_OK : st;
-    const int64_t nkb = K / 128;
-    hipStream_t s = (hipStream_t)stream;
-    // M <= 64: the decode kernels (B streamed once per launch, the LHS staged
-    // per wave 16 rows at a time). Where their LDS staging does not fit the
-    // shape, the older decode kernels keep M <= 24 and short K (< 16 blocks:
-    // a split-K launch pair costs more than it saves); the rest, and all
-    // larger M, go to the tile kernel, split over K when its tiles are few.
-    const bool forced_tiles = tile_override() == 1 || tile_override() == 2 || tile_override() == 4;
-    const int64_t decode_max_m = tile_override() == 13 ? 16 : 64;
-    if (M <= decode_max_m && !forced_tiles) {
-        st = launch_decode(p, s, M <= 24 || nkb < 16 || tile_override() == 14);
-        if (st != kDecodeDeclined)
-            return st;
-    }
-    if (!offsets_fit(lda, ldb, sa_stride_m))
-        return DG_ERR_UNSUPPORTED;
-    const bool wide_n = N % 256 == 0;
-    switch (tile_override()) {
-    case 1: return launch_tiles<dgk::kDense, CfgDense4>(p, 1, dev.cus, s);
-    case 2: return launch_tiles<dgk::kDense, CfgNarrow>(p, 1, dev.cus, s);
-    case 4: return launch_tiles<dgk::kDense, CfgDense>(p, 1, dev.cus, s);
-    case 15: return wide_n ? launch_dense<CfgBig>(p, dev.cus, s) : launch_dense<CfgDense>(p, dev.cus, s);
-    default:
-        return launch_dense_auto(p, dev.cus, s);
-    }
+        return (dg_status)(st == kEmptyProblem ? DG_OK : st);
+    Ctx c;
+    c.cus = dev.cus;
+    c.stream = (hipStream_t)stream;
+    c.ws = (uint8_t *)workspace;
+    c.ws_bytes = workspace ? (size_t)workspace_bytes : 0;
+    return (dg_status)dense_dispatch(p, c);
 }
 
-int dg_fp8_grouped_gemm_contiguous(const void *A, int64_t lda, const float *sA, int64_t sa_stride_m,
+int64_t dg_fp8_gemm_nt_workspace_bytes(int64_t M, int64_t N, int64_t K)
+{
+    int st = check_common_shape(M, N, K);
+    if (st != DG_OK)
+        return -st;
+    if (M == 0 || N == 0)
+        return 0;
+    DeviceInfo dev;
+    if ((st = current_device(dev)) != DG_OK)
+        return -st;
+    dgk::Params p = {};
+    p.lda = K; p.ldb = K; p.ldd = N;
+    p.sa_m = 1; p.sa_kb = M; p.sb_nb = K / 128; p.sb_kb = 1;  // the generator's (contiguous) layouts
+    p.M = (int)M; p.N = (int)N; p.K = (int)K; p.G = 1;
+    Ctx c;
+    c.cus = dev.cus;
+    c.dry = true;
+    st = dense_dispatch(p, c);
+    return st == DG_OK ? (int64_t)c.need : -st;
+}
+
+dg_status dg_fp8_grouped_gemm_contiguous(const void *A, int64_t lda, const float *sA, int64_t sa_stride_m,
                                    int64_t sa_stride_kb, const void *B, int64_t ldb, int64_t b_stride_g,
                                    const float *sB, int64_t sb_stride_g, int64_t sb_stride_nb, int64_t sb_stride_kb,
                                    const int32_t *expert_ids, void *D, int64_t ldd, int64_t M_total, int64_t N,
                                    int64_t K, int64_t G, void *stream)
 {
-    return contiguous_impl(A, lda, sA, sa_stride_m, sa_stride_kb, B, ldb, b_stride_g, sB, sb_stride_g,
+    return (dg_status)contiguous_impl(A, lda, sA, sa_stride_m, sa_stride_kb, B, ldb, b_stride_g, sB, sb_stride_g,
                            sb_stride_nb, sb_stride_kb, expert_ids, nullptr, D, ldd, M_total, M_total, N, K, G,
                            stream);
 }
 
-int dg_fp8_grouped_gemm_contiguous_to_tokens(const void *A, int64_t lda, const float *sA, int64_t sa_stride_m,
+dg_status dg_fp8_grouped_gemm_contiguous_to_tokens(const void *A, int64_t lda, const float *sA, int64_t sa_stride_m,
                                              int64_t sa_stride_kb, const void *B, int64_t ldb, int64_t b_stride_g,
                                              const float *sB, int64_t sb_stride_g, int64_t sb_stride_nb,
                                              int64_t sb_stride_kb, const int32_t *expert_ids,
@@ -851,12 +958,12 @@ int dg_fp8_grouped_gemm_contiguous_to_tokens(const void *A, int64_t lda, const f
 {
     if (M_total > 0 && N > 0 && G > 0 && T > 0 && !token_of_row)
         return DG_ERR_NULL_POINTER;
-    return contiguous_impl(A, lda, sA, sa_stride_m, sa_stride_kb, B, ldb, b_stride_g, sB, sb_stride_g,
+    return (dg_status)contiguous_impl(A, lda, sA, sa_stride_m, sa_stride_kb, B, ldb, b_stride_g, sB, sb_stride_g,
                            sb_stride_nb, sb_stride_kb, expert_ids, token_of_row, out, ldo, T, M_total, N, K, G,
                            stream, 0, layout);
 }
 
-int dg_fp8_grouped_gemm_contiguous_layout(const void *A, int64_t lda, const float *sA, int64_t sa_stride_m,
+dg_status dg_fp8_grouped_gemm_contiguous_layout(const void *A, int64_t lda, const float *sA, int64_t sa_stride_m,
                                           int64_t sa_stride_kb, const void *B, int64_t ldb, int64_t b_stride_g,
                                           const float *sB, int64_t sb_stride_g, int64_t sb_stride_nb,
                                           int64_t sb_stride_kb, const int32_t *expert_ids, const int32_t *layout,
@@ -865,23 +972,62 @@ int dg_fp8_grouped_gemm_contiguous_layout(const void *A, int64_t lda, const floa
 {
     if (M_total > 0 && N > 0 && G > 0 && !layout)
         return DG_ERR_NULL_POINTER;
-    return contiguous_impl(A, lda, sA, sa_stride_m, sa_stride_kb, B, ldb, b_stride_g, sB, sb_stride_g,
+    return (dg_status)contiguous_impl(A, lda, sA, sa_stride_m, sa_stride_kb, B, ldb, b_stride_g, sB, sb_stride_g,
                            sb_stride_nb, sb_stride_kb, expert_ids, nullptr, D, ldd, M_total, M_total, N, K, G,
                            stream, 0, layout);
 }
 
-int dg_fp8_grouped_gemm_masked(const void *A, int64_t lda, int64_t a_stride_g, const float *sA, int64_t sa_stride_g,
+dg_status dg_fp8_grouped_gemm_contiguous_ws(const void *A, int64_t lda, const float *sA, int64_t sa_stride_m,
+                                             int64_t sa_stride_kb, const void *B, int64_t ldb, int64_t b_stride_g,
+                                             const float *sB, int64_t sb_stride_g, int64_t sb_stride_nb,
+                                             int64_t sb_stride_kb, const int32_t *expert_ids,
+                                             const int32_t *token_of_row, const int32_t *layout, void *D,
+                                             int64_t ldd, int64_t T, int64_t M_total, int64_t N, int64_t K,
+                                             int64_t G, void *workspace, int64_t workspace_bytes, void *stream)
+{
+    return (dg_status)contiguous_impl(A, lda, sA, sa_stride_m, sa_stride_kb, B, ldb, b_stride_g, sB, sb_stride_g,
+                                      sb_stride_nb, sb_stride_kb, expert_ids, token_of_row, D, ldd,
+                                      token_of_row ? T : M_total, M_total, N, K, G, stream, 0, layout, workspace,
+                                      workspace_bytes);
+}
+
+int64_t dg_fp8_grouped_gemm_contiguous_workspace_bytes(int64_t M_total, int64_t N, int64_t K, int64_t G)
+{
+    int st = check_common_shape(M_total, N, K);
+    if (st != DG_OK)
+        return -st;
+    if (G < 0 || M_total % 128 != 0)
+        return -DG_ERR_BAD_SHAPE;
+    if (G > kInt32Max)
+        return -DG_ERR_UNSUPPORTED;
+    if (M_total == 0 || N == 0 || G == 0)
+        return 0;
+    DeviceInfo dev;
+    if ((st = current_device(dev)) != DG_OK)
+        return -st;
+    dgk::Params p = {};
+    p.lda = K; p.ldb = K; p.ldd = N; p.b_stride_g = N * K;
+    p.sa_m = 1; p.sa_kb = M_total; p.sb_nb = K / 128; p.sb_kb = 1; p.sb_g = (N / 128) * (K / 128);
+    p.M = (int)M_total; p.N = (int)N; p.K = (int)K; p.G = (int)G;
+    Ctx c;
+    c.cus = dev.cus;
+    c.dry = true;
+    st = contiguous_dispatch(p, c, false, 0);
+    return st == DG_OK ? (int64_t)c.need : -st;
+}
+
+dg_status dg_fp8_grouped_gemm_masked(const void *A, int64_t lda, int64_t a_stride_g, const float *sA, int64_t sa_stride_g,
                                int64_t sa_stride_m, int64_t sa_stride_kb, const void *B, int64_t ldb,
                                int64_t b_stride_g, const float *sB, int64_t sb_stride_g, int64_t sb_stride_nb,
                                int64_t sb_stride_kb, const int32_t *masked_m, void *D, int64_t ldd,
                                int64_t d_stride_g, int64_t G, int64_t M_max, int64_t N, int64_t K, void *stream)
 {
-    return masked_impl(A, lda, a_stride_g, sA, sa_stride_g, sa_stride_m, sa_stride_kb, B, ldb, b_stride_g, sB,
+    return (dg_status)masked_impl(A, lda, a_stride_g, sA, sa_stride_g, sa_stride_m, sa_stride_kb, B, ldb, b_stride_g, sB,
                        sb_stride_g, sb_stride_nb, sb_stride_kb, masked_m, D, ldd, d_stride_g, G, M_max, N, K, stream,
                        0);
 }
 
-int dg_fp8_grouped_gemm_masked_fmt(const void *A, int a_fmt, int64_t lda, int64_t a_stride_g, const float *sA,
+dg_status dg_fp8_grouped_gemm_masked_fmt(const void *A, int a_fmt, int64_t lda, int64_t a_stride_g, const float *sA,
                                    int64_t sa_stride_g, int64_t sa_stride_m, int64_t sa_stride_kb, const void *B,
                                    int b_fmt, int64_t ldb, int64_t b_stride_g, const float *sB, int64_t sb_stride_g,
                                    int64_t sb_stride_nb, int64_t sb_stride_kb, const int32_t *masked_m, void *D,
@@ -891,12 +1037,12 @@ int dg_fp8_grouped_gemm_masked_fmt(const void *A, int a_fmt, int64_t lda, int64_
     const int f = format_bits(a_fmt, b_fmt);
     if (f < 0)
         return DG_ERR_UNSUPPORTED;
-    return masked_impl(A, lda, a_stride_g, sA, sa_stride_g, sa_stride_m, sa_stride_kb, B, ldb, b_stride_g, sB,
+    return (dg_status)masked_impl(A, lda, a_stride_g, sA, sa_stride_g, sa_stride_m, sa_stride_kb, B, ldb, b_stride_g, sB,
                        sb_stride_g, sb_stride_nb, sb_stride_kb, masked_m, D, ldd, d_stride_g, G, M_max, N, K, stream,
                        f);
 }
 
-int dg_fp8_grouped_gemm_contiguous_fmt(const void *A, int a_fmt, int64_t lda, const float *sA, int64_t sa_stride_m,
+dg_status dg_fp8_grouped_gemm_contiguous_fmt(const void *A, int a_fmt, int64_t lda, const float *sA, int64_t sa_stride_m,
                                        int64_t sa_stride_kb, const void *B, int b_fmt, int64_t ldb,
                                        int64_t b_stride_g, const float *sB, int64_t sb_stride_g,
                                        int64_t sb_stride_nb, int64_t sb_stride_kb, const int32_t *expert_ids,
@@ -906,12 +1052,12 @@ int dg_fp8_grouped_gemm_contiguous_fmt(const void *A, int a_fmt, int64_t lda, co
     const int f = format_bits(a_fmt, b_fmt);
     if (f < 0)
         return DG_ERR_UNSUPPORTED;
-    return contiguous_impl(A, lda, sA, sa_stride_m, sa_stride_kb, B, ldb, b_stride_g, sB, sb_stride_g,
+    return (dg_status)contiguous_impl(A, lda, sA, sa_stride_m, sa_stride_kb, B, ldb, b_stride_g, sB, sb_stride_g,
                            sb_stride_nb, sb_stride_kb, expert_ids, nullptr, D, ldd, M_total, M_total, N, K, G,
                            stream, f);
 }
 
-int dg_fp8_gemm_nt_fmt(const void *A, int a_fmt, int64_t lda, const float *sA, int64_t sa_stride_m,
+dg_status dg_fp8_gemm_nt_fmt(const void *A, int a_fmt, int64_t lda, const float *sA, int64_t sa_stride_m,
                        int64_t sa_stride_kb, const void *B, int b_fmt, int64_t ldb, const float *sB,
                        int64_t sb_stride_nb, int64_t sb_stride_kb, void *D, int64_t ldd, int64_t M, int64_t N,
                        int64_t K, void *stream)
@@ -919,32 +1065,34 @@ int dg_fp8_gemm_nt_fmt(const void *A, int a_fmt, int64_t lda, const float *sA, i
     if ((a_fmt != DG_FP8_E4M3 && a_fmt != DG_FP8_E5M2) || (b_fmt != DG_FP8_E4M3 && b_fmt != DG_FP8_E5M2))
         return DG_ERR_UNSUPPORTED;
     if (a_fmt == DG_FP8_E4M3 && b_fmt == DG_FP8_E4M3)
-        return dg_fp8_gemm_nt(A, lda, sA, sa_stride_m, sa_stride_kb, B, ldb, sB, sb_stride_nb, sb_stride_kb, D,
+        return (dg_status)dg_fp8_gemm_nt(A, lda, sA, sa_stride_m, sa_stride_kb, B, ldb, sB, sb_stride_nb, sb_stride_kb, D,
                               ldd, M, N, K, stream);
     dgk::Params p;
     DeviceInfo dev;
     int st = dense_setup(A, lda, sA, sa_stride_m, sa_stride_kb, B, ldb, sB, sb_stride_nb, sb_stride_kb, D, ldd,
                          M, N, K, p, dev);
     if (st != DG_OK)
-        return st == kEmptyProblem ? DG_OK : st;
+        return (dg_status)(st == kEmptyProblem ? DG_OK : st);
     if (!offsets_fit(lda, ldb, sa_stride_m))
         return DG_ERR_UNSUPPORTED;
-    hipStream_t s = (hipStream_t)stream;
+    Ctx c;  // no workspace: never split over K
+    c.cus = dev.cus;
+    c.stream = (hipStream_t)stream;
     // Formats other than e4m3 x e4m3 run on the tile kernel at every M.
     switch ((a_fmt == DG_FP8_E5M2 ? 1 : 0) | (b_fmt == DG_FP8_E5M2 ? 2 : 0)) {
-    case 1: return launch_dense_auto<1>(p, dev.cus, s);
-    case 2: return launch_dense_auto<2>(p, dev.cus, s);
-    default: return launch_dense_auto<3>(p, dev.cus, s);
+    case 1: return (dg_status)launch_dense_auto<1>(p, c);
+    case 2: return (dg_status)launch_dense_auto<2>(p, c);
+    default: return (dg_status)launch_dense_auto<3>(p, c);
     }
 }
 
-int dg_fp8_quantize_1x128(const void *X, int x_dtype, int64_t ldx, void *Q, int64_t ldq, float *S,
+dg_status dg_fp8_quantize_1x128(const void *X, int x_dtype, int64_t ldx, void *Q, int64_t ldq, float *S,
                           int64_t s_stride_m, int64_t s_stride_kb, int64_t M, int64_t K, void *stream)
 {
-    return quantize_impl(X, x_dtype, ldx, M, nullptr, Q, ldq, S, s_stride_m, s_stride_kb, M, K, stream);
+    return (dg_status)(quantize_impl(X, x_dtype, ldx, M, nullptr, Q, ldq, S, s_stride_m, s_stride_kb, M, K, stream));
 }
 
-int dg_fp8_quantize_1x128_gather(const void *X, int x_dtype, int64_t ldx, int64_t x_rows,
+dg_status dg_fp8_quantize_1x128_gather(const void *X, int x_dtype, int64_t ldx, int64_t x_rows,
                                  const int32_t *src_rows, void *Q, int64_t ldq, float *S, int64_t s_stride_m,
                                  int64_t s_stride_kb, int64_t M, int64_t K, void *stream)
 {
@@ -954,7 +1102,7 @@ int dg_fp8_quantize_1x128_gather(const void *X, int x_dtype, int64_t ldx, int64_
         return DG_ERR_NULL_POINTER;
     if (src_rows && !aligned(src_rows, 4))
         return DG_ERR_MISALIGNED;
-    return quantize_impl(X, x_dtype, ldx, x_rows, src_rows, Q, ldq, S, s_stride_m, s_stride_kb, M, K, stream);
+    return (dg_status)(quantize_impl(X, x_dtype, ldx, x_rows, src_rows, Q, ldq, S, s_stride_m, s_stride_kb, M, K, stream));
 }
 
 int64_t dg_moe_contiguous_max_rows(int64_t T, int64_t G)
@@ -964,7 +1112,7 @@ int64_t dg_moe_contiguous_max_rows(int64_t T, int64_t G)
     return 128 * ((T + 127) / 128 + std::min(G, T));
 }
 
-int dg_moe_route_contiguous(const int32_t *expert_of_token, int64_t T, int64_t G, int32_t *row_of_token,
+dg_status dg_moe_route_contiguous(const int32_t *expert_of_token, int64_t T, int64_t G, int32_t *row_of_token,
                             int32_t *expert_ids, int32_t *token_of_row, int32_t *layout, int64_t M_cap,
                             void *stream)
 {
@@ -995,17 +1143,17 @@ int dg_moe_route_contiguous(const int32_t *expert_of_token, int64_t T, int64_t G
     DeviceInfo dev;
     int st = current_device(dev);
     if (st != DG_OK)
-        return st;
+        return (dg_status)(st);
     dgm::RouteParams p = {};
     p.expert_of_token = expert_of_token;
     p.T = (int)T; p.G = (int)G; p.M_cap = (int)M_cap;
     p.row_of_token = row_of_token; p.expert_ids = expert_ids; p.token_of_row = token_of_row; p.layout = layout;
     hipLaunchKernelGGL(dgm::route_contiguous_kernel, dim3(1), dim3(dgm::kRouteThreads), 0, (hipStream_t)stream, p);
     const hipError_t e = hipGetLastError();
-    return e == hipSuccess ? DG_OK : fail_hip(e);
+    return (dg_status)(e == hipSuccess ? DG_OK : fail_hip(e));
 }
 
-int dg_moe_unpermute(const void *D, int64_t ldd, int64_t d_rows, const int32_t *row_of_token, int64_t T,
+dg_status dg_moe_unpermute(const void *D, int64_t ldd, int64_t d_rows, const int32_t *row_of_token, int64_t T,
                      int64_t N, void *out, int64_t ldo, void *stream)
 {
     if (T < 0 || N < 0 || d_rows < 0 || N % 8 != 0)
@@ -1027,7 +1175,7 @@ int dg_moe_unpermute(const void *D, int64_t ldd, int64_t d_rows, const int32_t *
     DeviceInfo dev;
     int st = current_device(dev);
     if (st != DG_OK)
-        return st;
+        return (dg_status)(st);
     dgm::UnpermuteParams p = {};
     p.D = (const uint16_t *)D; p.ldd = ldd; p.d_rows = (int)d_rows;
     p.row_of_token = row_of_token; p.T = (int)T; p.N = (int)N;
@@ -1036,7 +1184,7 @@ int dg_moe_unpermute(const void *D, int64_t ldd, int64_t d_rows, const int32_t *
     hipLaunchKernelGGL(dgm::unpermute_kernel, dim3(groups), dim3(64 * dgm::kUnpermuteWaves), 0,
                        (hipStream_t)stream, p);
     const hipError_t e = hipGetLastError();
-    return e == hipSuccess ? DG_OK : fail_hip(e);
+    return (dg_status)(e == hipSuccess ? DG_OK : fail_hip(e));
 }
 
 }  // extern "C"

@@ -79,6 +79,54 @@ def dg_fp8_gemm_nt(a, sa, b, sb, d=None, stream=None):
     return d
 
 
+def _ws(workspace):
+    """(pointer, bytes) of a caller workspace: a device tensor or None."""
+    if workspace is None or workspace.numel() == 0:
+        return None, 0
+    if not workspace.is_cuda or not workspace.is_contiguous():
+        raise ValueError("workspace must be a contiguous device tensor")
+    return workspace.data_ptr(), workspace.numel() * workspace.element_size()
+
+
+def _query(n: int, where: str) -> int:
+    if n < 0:
+        raise DGError(-n, where)
+    return int(n)
+
+
+def dg_fp8_gemm_nt_workspace_bytes(M: int, N: int, K: int) -> int:
+    """Workspace bytes the fastest path of dg_fp8_gemm_nt_ws takes (0: none)."""
+    return _query(_lib.load().dg_fp8_gemm_nt_workspace_bytes(M, N, K), "dg_fp8_gemm_nt_workspace_bytes")
+
+
+def workspace(nbytes: int, device="cuda") -> torch.Tensor:
+    """A caller-owned workspace tensor of at least nbytes bytes (torch allocates it)."""
+    return torch.empty(max(int(nbytes), 0), dtype=torch.uint8, device=device)
+
+
+def dg_fp8_gemm_nt_ws(a, sa, b, sb, workspace, d=None, stream=None):
+    """dg_fp8_gemm_nt with a caller workspace (a uint8 device tensor, or None)
+    for its split-K path."""
+    _codes(a, "a", 2), _codes(b, "b", 2), _scales(sa, "sa", 2), _scales(sb, "sb", 2)
+    M, K = a.shape
+    N = b.shape[0]
+    if d is None:
+        d = torch.empty((M, N), dtype=torch.bfloat16, device=a.device)
+    if d.dtype != torch.bfloat16 or d.dim() != 2 or d.stride(-1) != 1:
+        raise TypeError("d must be a 2-D bfloat16 tensor with contiguous rows")
+    if b.shape[1] != K or tuple(d.shape) != (M, N):
+        raise ValueError("shape mismatch")
+    if tuple(sa.shape) != (M, K // BLOCK) or tuple(sb.shape) != (N // BLOCK, K // BLOCK):
+        raise ValueError("scale shape mismatch")
+    wp, wb = _ws(workspace)
+    lib = _lib.load()
+    st = lib.dg_fp8_gemm_nt_ws(_dev(a, "a"), a.stride(0), _dev(sa, "sa"), sa.stride(0), sa.stride(1),
+                               _dev(b, "b"), b.stride(0), _dev(sb, "sb"), sb.stride(0), sb.stride(1),
+                               _dev(d, "d"), d.stride(0), M, N, K, wp, wb, _stream(stream))
+    _check(st, "dg_fp8_gemm_nt_ws")
+    return d
+
+
 FORMATS = {"e4m3": 0, "e5m2": 1}   # DG_FP8_E4M3, DG_FP8_E5M2
 
 
@@ -181,6 +229,49 @@ def dg_fp8_grouped_gemm_contiguous_layout(a, sa, b, sb, expert_ids, layout, d=No
         _dev(expert_ids, "expert_ids"), _dev(layout, "layout"), _dev(d, "d"), d.stride(0),
         M_total, N, K, G, _stream(stream))
     _check(st, "dg_fp8_grouped_gemm_contiguous_layout")
+    return d
+
+
+def dg_fp8_grouped_gemm_contiguous_workspace_bytes(M_total: int, N: int, K: int, G: int) -> int:
+    """Workspace bytes the fastest path of dg_fp8_grouped_gemm_contiguous_ws takes (0: none)."""
+    return _query(_lib.load().dg_fp8_grouped_gemm_contiguous_workspace_bytes(M_total, N, K, G),
+                  "dg_fp8_grouped_gemm_contiguous_workspace_bytes")
+
+
+def dg_fp8_grouped_gemm_contiguous_ws(a, sa, b, sb, expert_ids, workspace, token_of_row=None, T=None, layout=None,
+                                      d=None, stream=None):
+    """The contiguous grouped GEMM with a caller workspace (uint8 device
+    tensor or None): segment offsets derived on the device when no layout is
+    given, the segments' last 128 rows split over K. With token_of_row the
+    rows go to d [T, N] in token order, else to d [M_total, N]."""
+    _codes(a, "a", 2), _codes(b, "b", 3), _scales(sa, "sa", 2), _scales(sb, "sb", 3)
+    M_total, K = a.shape
+    G, N, _ = b.shape
+    if expert_ids.dtype != torch.int32 or tuple(expert_ids.shape) != (M_total,) or expert_ids.stride(0) != 1:
+        raise ValueError("expert_ids must be a contiguous int32 [M_total] tensor")
+    if token_of_row is not None:
+        if token_of_row.dtype != torch.int32 or tuple(token_of_row.shape) != (M_total,):
+            raise ValueError("token_of_row must be int32 [M_total]")
+        if T is None:
+            raise ValueError("T (rows of the token-order output) is needed with token_of_row")
+    rows = M_total if token_of_row is None else T
+    if layout is not None and (layout.dtype != torch.int32 or tuple(layout.shape) != (G + 1,)):
+        raise ValueError("layout must be int32 [G+1]")
+    if tuple(sa.shape) != (M_total, K // BLOCK) or tuple(sb.shape) != (G, N // BLOCK, K // BLOCK):
+        raise ValueError("scale shape mismatch")
+    if d is None:
+        d = torch.empty((rows, N), dtype=torch.bfloat16, device=a.device)
+    if d.dtype != torch.bfloat16 or tuple(d.shape) != (rows, N) or d.stride(-1) != 1:
+        raise ValueError("d must be a bfloat16 [%d, N] tensor with contiguous rows" % rows)
+    wp, wb = _ws(workspace)
+    lib = _lib.load()
+    st = lib.dg_fp8_grouped_gemm_contiguous_ws(
+        _dev(a, "a"), a.stride(0), _dev(sa, "sa"), sa.stride(0), sa.stride(1),
+        _dev(b, "b"), b.stride(1), b.stride(0), _dev(sb, "sb"), sb.stride(0), sb.stride(1), sb.stride(2),
+        _dev(expert_ids, "expert_ids"), None if token_of_row is None else _dev(token_of_row, "token_of_row"),
+        None if layout is None else _dev(layout, "layout"), _dev(d, "d"), d.stride(0), rows,
+        M_total, N, K, G, wp, wb, _stream(stream))
+    _check(st, "dg_fp8_grouped_gemm_contiguous_ws")
     return d
 
 

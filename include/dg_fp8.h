@@ -31,10 +31,15 @@
  *     keeps one past return.
  *   - `stream` is a hipStream_t (NULL = the legacy default stream). The call
  *     validates its arguments on the host, enqueues its kernels and returns.
- *     It allocates nothing and does not synchronise, except for the split-K
- *     workspace that dg_fp8_gemm_nt (and _fmt) and the segment-tiled grouped
- *     GEMMs share (see dg_fp8_gemm_nt), and the small buffer of segment
- *     offsets that dg_fp8_grouped_gemm_contiguous derives (see there).
+ *     The library never allocates or frees device memory and never
+ *     synchronises a stream. Scratch memory (split-K partial sums, segment
+ *     offsets derived on the device) is the caller's: the *_ws entry points
+ *     take a workspace pointer and size (a caller workspace, 16-byte aligned:
+ *     bhfrc.com DeepGEMM article, §5.2), and the matching *_workspace_bytes
+ *     query says how much the fastest path takes. Calls without a workspace
+ *     take the paths that need none. Every call is therefore safe to capture
+ *     into a HIP graph: its kernels only read and write memory the caller
+ *     passed, at addresses fixed at capture (bhfrc.com §4.3).
  *   - Strides are in elements. e4m3 is one byte, so A/B strides are also byte
  *     strides; D strides count bf16 elements. Scale tables are addressed
  *     logically through explicit strides: sA[m, kb] = sA[m*sa_stride_m +
@@ -47,8 +52,9 @@
  *   - Shapes: K > 0 and K % 128 == 0; N % 128 == 0; M arbitrary (>= 0).
  *   - D must not overlap A, B, sA, sB or the routing arrays.
  *   - Results are deterministic: no atomics, a fixed reduction order.
- *   - Thread-safe; the global state is a per-device property cache and the
- *     per-stream split-K workspaces and offset buffers.
+ *   - Thread-safe: the only global state is a per-device property cache,
+ *     filled once under a lock. Calls that share a workspace must not run
+ *     concurrently (issue them on one stream, or give each its own).
  *
  * Errors: every error is detected on the host before anything is enqueued,
  * and D is left untouched. DG_ERR_HIP reports a failed launch; the HIP error
@@ -64,9 +70,9 @@
 extern "C" {
 #endif
 
-#define DG_ABI_VERSION 1
+#define DG_ABI_VERSION 2
 
-enum {
+typedef enum dg_status {
     DG_OK = 0,
     DG_ERR_NULL_POINTER = 1, /* a required pointer is NULL for a non-empty problem */
     DG_ERR_BAD_SHAPE = 2,    /* negative dim, K <= 0, K % 128, N % 128, M_total % 128 */
@@ -74,14 +80,14 @@ enum {
     DG_ERR_BAD_STRIDE = 4,   /* lda < K, ldb < K, ldd < N, negative or too small group stride */
     DG_ERR_UNSUPPORTED = 5,  /* current device is not gfx950, or a size exceeds int32 */
     DG_ERR_HIP = 6,          /* the HIP runtime failed (query or launch) */
-    DG_ERR_ALIASING = 7      /* D overlaps an input */
-};
+    DG_ERR_ALIASING = 7      /* D (or the workspace) overlaps an input or the output */
+} dg_status;
 
 /* Version of this ABI (DG_ABI_VERSION). */
 int dg_abi_version(void);
 
 /* Static, human-readable text for a status code (never NULL). */
-const char *dg_status_string(int status);
+const char *dg_status_string(dg_status status);
 
 /* hipError_t of the last DG_ERR_HIP returned on the calling thread (0 if none). */
 int dg_last_hip_error(void);
@@ -94,35 +100,55 @@ int dg_last_hip_error(void);
  * Operation as in the header comment (lpnh.cn §2.3; hotdry.top, fine-grained
  * scaling core design).
  *
- * Split-K: when M > 64 (or 24 < M <= 64 where the small-M kernel's LDS
- * staging does not fit and K >= 2048) and the output tiles would fill at most half of the
- * GPU's CUs (e.g. M up to ~2000 at N = 4096), each tile's K blocks are split
- * over up to 8 work items that write fp32 partial sums to a device workspace,
- * and a second kernel adds them in a fixed order. The workspace (slices x M x
- * N x 4 bytes) belongs to the library: one per (device, stream), allocated
- * with hipMalloc on the first such call on that stream and regrown (after
- * hipStreamSynchronize on that stream) when a call needs more. While the
- * stream is being captured into a graph nothing is allocated: a call whose
- * stream has no large-enough workspace yet runs without the split (so one
- * eager call on the capture stream beforehand puts the split in the graph).
- * A captured graph keeps using the workspace it was captured with: a later
- * call on that stream that needs a larger one frees it, so make the largest
- * call before capturing, or capture again after such a call.
- * Concurrent calls on different streams use different workspaces. If the
- * allocation fails the call runs without the split.
+ * Without a workspace this call never splits a tile's K loop: medium M
+ * (64 < M up to ~2000 at N = 4096, where the output tiles would fill at most
+ * half of the CUs) then runs with few busy CUs. dg_fp8_gemm_nt_ws gives it
+ * the workspace for the split-K path.
  *
  * Large grids: when the 256x256 output tiles fill the CUs but leave a last
  * round at most half full, the call is issued as two launches on the same
  * stream, the whole-round part of the columns (else rows) on 256x256 tiles
- * and the remaining strip on smaller tiles (split over K if that strip alone
- * is small). The cut depends only on the shape and the CU count.
+ * and the remaining strip on smaller tiles. The cut depends only on the
+ * shape and the CU count.
  */
-int dg_fp8_gemm_nt(const void *A, int64_t lda,
-                   const float *sA, int64_t sa_stride_m, int64_t sa_stride_kb,
-                   const void *B, int64_t ldb,
-                   const float *sB, int64_t sb_stride_nb, int64_t sb_stride_kb,
-                   void *D, int64_t ldd,
-                   int64_t M, int64_t N, int64_t K, void *stream);
+dg_status dg_fp8_gemm_nt(const void *A, int64_t lda,
+                         const float *sA, int64_t sa_stride_m, int64_t sa_stride_kb,
+                         const void *B, int64_t ldb,
+                         const float *sB, int64_t sb_stride_nb, int64_t sb_stride_kb,
+                         void *D, int64_t ldd,
+                         int64_t M, int64_t N, int64_t K, void *stream);
+
+/*
+ * dg_fp8_gemm_nt with a caller workspace for its split-K path.
+ *   workspace        device memory owned by the caller, 16-byte aligned, or NULL
+ *   workspace_bytes  its size in bytes (>= 0)
+ * When the output tiles would fill at most half of the CUs (M > 64, or
+ * 24 < M <= 64 where the small-M kernel's LDS staging does not fit and
+ * K >= 2048), each tile's K blocks are split over up to 8 work items that
+ * write fp32 partial sums (slices x M x N x 4 bytes) to the workspace, and a
+ * second kernel adds the slices in a fixed order (deterministic). A workspace
+ * smaller than dg_fp8_gemm_nt_workspace_bytes takes as many slices as it
+ * holds (none below two: then this is dg_fp8_gemm_nt). The split only
+ * regroups the fp32 additions; results stay within the oracle tolerance.
+ * The workspace must not overlap D or an input (DG_ERR_ALIASING); its
+ * contents on entry do not matter and are garbage on return. Calls that use
+ * one workspace must be ordered (one stream): a later call overwrites it.
+ */
+dg_status dg_fp8_gemm_nt_ws(const void *A, int64_t lda,
+                            const float *sA, int64_t sa_stride_m, int64_t sa_stride_kb,
+                            const void *B, int64_t ldb,
+                            const float *sB, int64_t sb_stride_nb, int64_t sb_stride_kb,
+                            void *D, int64_t ldd,
+                            int64_t M, int64_t N, int64_t K,
+                            void *workspace, int64_t workspace_bytes, void *stream);
+
+/*
+ * Workspace bytes the fastest path of dg_fp8_gemm_nt_ws takes for this shape
+ * on the current device (0: that path needs none), assuming operands with
+ * K-contiguous rows (lda = ldb = K). A negative value is -dg_status: a bad
+ * shape, or a device that is not gfx950. Launches nothing.
+ */
+int64_t dg_fp8_gemm_nt_workspace_bytes(int64_t M, int64_t N, int64_t K);
 
 /* Operand formats of dg_fp8_gemm_nt_fmt. */
 #define DG_FP8_E4M3 0
@@ -137,15 +163,15 @@ int dg_fp8_gemm_nt(const void *A, int64_t lda,
  * of dg_fp8_gemm_nt; a_fmt / b_fmt are DG_FP8_E4M3 or DG_FP8_E5M2 (else
  * DG_ERR_UNSUPPORTED). Infinity and NaN codes in an operand give unspecified
  * results. With both operands e4m3 this is dg_fp8_gemm_nt; every other
- * combination runs on the tile kernel at every M (split over K, with the
- * same workspace rules, when its tiles are few).
+ * combination runs on the tile kernel at every M (never split over K: this
+ * call takes no workspace).
  */
-int dg_fp8_gemm_nt_fmt(const void *A, int a_fmt, int64_t lda,
-                       const float *sA, int64_t sa_stride_m, int64_t sa_stride_kb,
-                       const void *B, int b_fmt, int64_t ldb,
-                       const float *sB, int64_t sb_stride_nb, int64_t sb_stride_kb,
-                       void *D, int64_t ldd,
-                       int64_t M, int64_t N, int64_t K, void *stream);
+dg_status dg_fp8_gemm_nt_fmt(const void *A, int a_fmt, int64_t lda,
+                             const float *sA, int64_t sa_stride_m, int64_t sa_stride_kb,
+                             const void *B, int b_fmt, int64_t ldb,
+                             const float *sB, int64_t sb_stride_nb, int64_t sb_stride_kb,
+                             void *D, int64_t ldd,
+                             int64_t M, int64_t N, int64_t K, void *stream);
 
 /*
  * Grouped GEMM, contiguous layout (MoE): the rows of all experts are stacked
@@ -162,25 +188,19 @@ int dg_fp8_gemm_nt_fmt(const void *A, int a_fmt, int64_t lda,
  * Layout contract: M_total % 128 == 0 and within every aligned 128-row block
  * all ids in [0, G) are equal (segments padded to 128). A block's expert is
  * the largest id in the block; a row whose id differs from it is not written.
- * Tiling: for e4m3 operands with N % 256 == 0, G <= 128 and at most 4096
- * blocks of 128 rows, a one-workgroup kernel first derives each expert's
- * segment offsets from expert_ids on the device, into a per-stream buffer of
- * (G + 2) int32 kept by the library (allocated like the split-K workspace of
- * dg_fp8_gemm_nt, never during graph capture). The GEMM then tiles along the
- * segments as dg_fp8_grouped_gemm_contiguous_layout does, tails split over K
- * included. If the block experts are not in ascending order (padding blocks
- * anywhere are fine), the derivation says so on the device and a uniform-grid
- * launch covers the rows instead. Either way the rows written are the same;
- * their values differ only in the grouping of the fp32 sums of split tails.
+ * Tiling: this call takes no workspace, so its tiles cover the rows
+ * uniformly (256-row tiles that straddle two experts run one K loop per
+ * expert). dg_fp8_grouped_gemm_contiguous_ws with a workspace instead
+ * derives the experts' segment offsets on the device and tiles along them.
  */
-int dg_fp8_grouped_gemm_contiguous(const void *A, int64_t lda,
-                                   const float *sA, int64_t sa_stride_m, int64_t sa_stride_kb,
-                                   const void *B, int64_t ldb, int64_t b_stride_g,
-                                   const float *sB, int64_t sb_stride_g, int64_t sb_stride_nb,
-                                   int64_t sb_stride_kb,
-                                   const int32_t *expert_ids,
-                                   void *D, int64_t ldd,
-                                   int64_t M_total, int64_t N, int64_t K, int64_t G, void *stream);
+dg_status dg_fp8_grouped_gemm_contiguous(const void *A, int64_t lda,
+                                         const float *sA, int64_t sa_stride_m, int64_t sa_stride_kb,
+                                         const void *B, int64_t ldb, int64_t b_stride_g,
+                                         const float *sB, int64_t sb_stride_g, int64_t sb_stride_nb,
+                                         int64_t sb_stride_kb,
+                                         const int32_t *expert_ids,
+                                         void *D, int64_t ldd,
+                                         int64_t M_total, int64_t N, int64_t K, int64_t G, void *stream);
 
 /*
  * The contiguous grouped GEMM given each expert's segment offsets as well
@@ -194,23 +214,18 @@ int dg_fp8_grouped_gemm_contiguous(const void *A, int64_t lda,
  * experts. Result and other arguments as dg_fp8_grouped_gemm_contiguous;
  * 1 <= G <= 1024. A layout that does not match expert_ids leaves rows
  * unwritten (no fault).
- * The last 128 rows of the segments may be split over K (at most 8 slices of
- * at least 4 K blocks, the count chosen on the device from the number of such
- * segments) when the tails would fill under two rounds of the CUs; those rows
- * then differ from the unsplit sum only in the grouping of the fp32
- * additions. The fp32 partials go to the stream's split-K workspace (slices x
- * G x 128 x N x 4 bytes) under the rules of dg_fp8_gemm_nt: allocated outside
- * graph capture, so one eager call on a capture stream puts the split in the
- * graph; without it the call runs unsplit.
+ * This call takes no workspace: the segments' last 128 rows run on 256-row
+ * tiles in the same launch. dg_fp8_grouped_gemm_contiguous_ws with a
+ * workspace splits them over K (see there).
  */
-int dg_fp8_grouped_gemm_contiguous_layout(const void *A, int64_t lda,
-                                          const float *sA, int64_t sa_stride_m, int64_t sa_stride_kb,
-                                          const void *B, int64_t ldb, int64_t b_stride_g,
-                                          const float *sB, int64_t sb_stride_g, int64_t sb_stride_nb,
-                                          int64_t sb_stride_kb,
-                                          const int32_t *expert_ids, const int32_t *layout,
-                                          void *D, int64_t ldd,
-                                          int64_t M_total, int64_t N, int64_t K, int64_t G, void *stream);
+dg_status dg_fp8_grouped_gemm_contiguous_layout(const void *A, int64_t lda,
+                                                const float *sA, int64_t sa_stride_m, int64_t sa_stride_kb,
+                                                const void *B, int64_t ldb, int64_t b_stride_g,
+                                                const float *sB, int64_t sb_stride_g, int64_t sb_stride_nb,
+                                                int64_t sb_stride_kb,
+                                                const int32_t *expert_ids, const int32_t *layout,
+                                                void *D, int64_t ldd,
+                                                int64_t M_total, int64_t N, int64_t K, int64_t G, void *stream);
 
 /*
  * The contiguous grouped GEMM written straight to token order: row r of the
@@ -219,10 +234,8 @@ int dg_fp8_grouped_gemm_contiguous_layout(const void *A, int64_t lda,
  * This folds dg_moe_unpermute into the GEMM's epilogue.
  *   token_of_row [M_total] int32 (device), as written by dg_moe_route_contiguous
  *   layout [G + 1] int32 (device) or NULL: segment offsets as in
- *   dg_fp8_grouped_gemm_contiguous_layout (then tiles follow the segments,
- *   and the segments' last 128 rows may be split over K as described there);
- *   with NULL the offsets are derived from expert_ids on the device as in
- *   dg_fp8_grouped_gemm_contiguous
+ *   dg_fp8_grouped_gemm_contiguous_layout (then tiles follow the segments);
+ *   with NULL the tiles cover the rows uniformly
  *   out [T, N] bf16, row stride ldo: rows of tokens that no row names (dropped
  *   tokens) are NOT written.
  * Precondition: no token appears twice in token_of_row (the routing call
@@ -230,29 +243,79 @@ int dg_fp8_grouped_gemm_contiguous_layout(const void *A, int64_t lda,
  * Other arguments, constraints and errors as dg_fp8_grouped_gemm_contiguous,
  * with out/ldo/T in place of D/ldd/M_total for the output.
  */
-int dg_fp8_grouped_gemm_contiguous_to_tokens(const void *A, int64_t lda,
+dg_status dg_fp8_grouped_gemm_contiguous_to_tokens(const void *A, int64_t lda,
+                                                   const float *sA, int64_t sa_stride_m, int64_t sa_stride_kb,
+                                                   const void *B, int64_t ldb, int64_t b_stride_g,
+                                                   const float *sB, int64_t sb_stride_g, int64_t sb_stride_nb,
+                                                   int64_t sb_stride_kb,
+                                                   const int32_t *expert_ids, const int32_t *token_of_row,
+                                                   const int32_t *layout,
+                                                   void *out, int64_t ldo, int64_t T,
+                                                   int64_t M_total, int64_t N, int64_t K, int64_t G, void *stream);
+
+/*
+ * The contiguous grouped GEMM (all three forms above) with a caller
+ * workspace for its faster paths.
+ *   token_of_row [M_total] int32 or NULL: as in _to_tokens (D is then out
+ *   [T, N]); NULL writes row r to row r of D [M_total, N] (T is ignored)
+ *   layout [G + 1] int32 or NULL: segment offsets as in _layout
+ *   workspace        device memory owned by the caller, 16-byte aligned, or NULL
+ *   workspace_bytes  its size in bytes (>= 0)
+ * With the workspace:
+ *   - without a layout (e4m3, N % 256 == 0, G <= 128, at most 4096 blocks of
+ *     128 rows), a one-workgroup kernel first derives each expert's segment
+ *     offsets from expert_ids into the workspace's first bytes ((G + 2)
+ *     int32, rounded up to 256 bytes), and the GEMM tiles along the segments
+ *     as with a layout. If the block experts are not in ascending order
+ *     (padding blocks anywhere are fine), the derivation says so on the
+ *     device and a uniform-grid launch covers the rows instead; either way
+ *     the rows written are the same;
+ *   - the segments' last 128 rows (a segment whose size is an odd multiple
+ *     of 128) are split over K when those tails would fill under two rounds
+ *     of the CUs: at most 8 slices of at least 4 K blocks, the count chosen
+ *     on the device from the number of such segments, fp32 partials (slices
+ *     x G x 128 x N x 4 bytes, after the offsets) added in slice order by a
+ *     reduction kernel. Those rows then differ from the unsplit sum only in
+ *     the grouping of the fp32 additions (within the oracle tolerance,
+ *     deterministic).
+ * A workspace smaller than dg_fp8_grouped_gemm_contiguous_workspace_bytes
+ * takes the paths it holds (fewer slices, or none). The workspace must not
+ * overlap D or an input; its contents on entry do not matter. Calls that use
+ * one workspace must be ordered (one stream).
+ * Other arguments, constraints and errors as the calls above.
+ */
+dg_status dg_fp8_grouped_gemm_contiguous_ws(const void *A, int64_t lda,
                                              const float *sA, int64_t sa_stride_m, int64_t sa_stride_kb,
                                              const void *B, int64_t ldb, int64_t b_stride_g,
                                              const float *sB, int64_t sb_stride_g, int64_t sb_stride_nb,
                                              int64_t sb_stride_kb,
                                              const int32_t *expert_ids, const int32_t *token_of_row,
                                              const int32_t *layout,
-                                             void *out, int64_t ldo, int64_t T,
-                                             int64_t M_total, int64_t N, int64_t K, int64_t G, void *stream);
+                                             void *D, int64_t ldd, int64_t T,
+                                             int64_t M_total, int64_t N, int64_t K, int64_t G,
+                                             void *workspace, int64_t workspace_bytes, void *stream);
+
+/*
+ * Workspace bytes the fastest path of dg_fp8_grouped_gemm_contiguous_ws takes
+ * for this shape on the current device (derived offsets plus split tails; a
+ * call given a layout needs no more), assuming K-contiguous operand rows.
+ * 0: none is used. A negative value is -dg_status (bad shape, not gfx950).
+ */
+int64_t dg_fp8_grouped_gemm_contiguous_workspace_bytes(int64_t M_total, int64_t N, int64_t K, int64_t G);
 
 /*
  * The contiguous grouped GEMM with a choice of fp8 format per operand
  * (a_fmt / b_fmt: DG_FP8_E4M3 or DG_FP8_E5M2, as in dg_fp8_gemm_nt_fmt);
  * otherwise identical to dg_fp8_grouped_gemm_contiguous.
  */
-int dg_fp8_grouped_gemm_contiguous_fmt(const void *A, int a_fmt, int64_t lda,
-                                       const float *sA, int64_t sa_stride_m, int64_t sa_stride_kb,
-                                       const void *B, int b_fmt, int64_t ldb, int64_t b_stride_g,
-                                       const float *sB, int64_t sb_stride_g, int64_t sb_stride_nb,
-                                       int64_t sb_stride_kb,
-                                       const int32_t *expert_ids,
-                                       void *D, int64_t ldd,
-                                       int64_t M_total, int64_t N, int64_t K, int64_t G, void *stream);
+dg_status dg_fp8_grouped_gemm_contiguous_fmt(const void *A, int a_fmt, int64_t lda,
+                                             const float *sA, int64_t sa_stride_m, int64_t sa_stride_kb,
+                                             const void *B, int b_fmt, int64_t ldb, int64_t b_stride_g,
+                                             const float *sB, int64_t sb_stride_g, int64_t sb_stride_nb,
+                                             int64_t sb_stride_kb,
+                                             const int32_t *expert_ids,
+                                             void *D, int64_t ldd,
+                                             int64_t M_total, int64_t N, int64_t K, int64_t G, void *stream);
 
 /*
  * Grouped GEMM, masked layout (MoE decode): every expert owns a fixed block
@@ -268,30 +331,30 @@ int dg_fp8_grouped_gemm_contiguous_fmt(const void *A, int a_fmt, int64_t lda,
  * Group g writes rows m < clamp(masked_m[g], 0, M_max); all other rows of D
  * are NOT written.
  */
-int dg_fp8_grouped_gemm_masked(const void *A, int64_t lda, int64_t a_stride_g,
-                               const float *sA, int64_t sa_stride_g, int64_t sa_stride_m,
-                               int64_t sa_stride_kb,
-                               const void *B, int64_t ldb, int64_t b_stride_g,
-                               const float *sB, int64_t sb_stride_g, int64_t sb_stride_nb,
-                               int64_t sb_stride_kb,
-                               const int32_t *masked_m,
-                               void *D, int64_t ldd, int64_t d_stride_g,
-                               int64_t G, int64_t M_max, int64_t N, int64_t K, void *stream);
+dg_status dg_fp8_grouped_gemm_masked(const void *A, int64_t lda, int64_t a_stride_g,
+                                     const float *sA, int64_t sa_stride_g, int64_t sa_stride_m,
+                                     int64_t sa_stride_kb,
+                                     const void *B, int64_t ldb, int64_t b_stride_g,
+                                     const float *sB, int64_t sb_stride_g, int64_t sb_stride_nb,
+                                     int64_t sb_stride_kb,
+                                     const int32_t *masked_m,
+                                     void *D, int64_t ldd, int64_t d_stride_g,
+                                     int64_t G, int64_t M_max, int64_t N, int64_t K, void *stream);
 
 /*
  * The masked grouped GEMM with a choice of fp8 format per operand (a_fmt /
  * b_fmt: DG_FP8_E4M3 or DG_FP8_E5M2, as in dg_fp8_gemm_nt_fmt); otherwise
  * identical to dg_fp8_grouped_gemm_masked.
  */
-int dg_fp8_grouped_gemm_masked_fmt(const void *A, int a_fmt, int64_t lda, int64_t a_stride_g,
-                                   const float *sA, int64_t sa_stride_g, int64_t sa_stride_m,
-                                   int64_t sa_stride_kb,
-                                   const void *B, int b_fmt, int64_t ldb, int64_t b_stride_g,
-                                   const float *sB, int64_t sb_stride_g, int64_t sb_stride_nb,
-                                   int64_t sb_stride_kb,
-                                   const int32_t *masked_m,
-                                   void *D, int64_t ldd, int64_t d_stride_g,
-                                   int64_t G, int64_t M_max, int64_t N, int64_t K, void *stream);
+dg_status dg_fp8_grouped_gemm_masked_fmt(const void *A, int a_fmt, int64_t lda, int64_t a_stride_g,
+                                         const float *sA, int64_t sa_stride_g, int64_t sa_stride_m,
+                                         int64_t sa_stride_kb,
+                                         const void *B, int b_fmt, int64_t ldb, int64_t b_stride_g,
+                                         const float *sB, int64_t sb_stride_g, int64_t sb_stride_nb,
+                                         int64_t sb_stride_kb,
+                                         const int32_t *masked_m,
+                                         void *D, int64_t ldd, int64_t d_stride_g,
+                                         int64_t G, int64_t M_max, int64_t N, int64_t K, void *stream);
 
 /* Element types of the quantiser's input. */
 #define DG_DTYPE_F32 0
@@ -322,10 +385,10 @@ int dg_fp8_grouped_gemm_masked_fmt(const void *A, int a_fmt, int64_t lda, int64_
  * DG_ERR_UNSUPPORTED for an unknown x_dtype. Deterministic; M = 0 returns
  * DG_OK without launching. Asynchronous on `stream`, allocates nothing.
  */
-int dg_fp8_quantize_1x128(const void *X, int x_dtype, int64_t ldx,
-                          void *Q, int64_t ldq,
-                          float *S, int64_t s_stride_m, int64_t s_stride_kb,
-                          int64_t M, int64_t K, void *stream);
+dg_status dg_fp8_quantize_1x128(const void *X, int x_dtype, int64_t ldx,
+                                void *Q, int64_t ldq,
+                                float *S, int64_t s_stride_m, int64_t s_stride_kb,
+                                int64_t M, int64_t K, void *stream);
 
 /*
  * The quantiser over a gathered row order: output row r quantises row
@@ -338,11 +401,11 @@ int dg_fp8_quantize_1x128(const void *X, int x_dtype, int64_t ldx,
  * Errors as dg_fp8_quantize_1x128; also DG_ERR_NULL_POINTER for a NULL
  * src_rows when M > 0, DG_ERR_BAD_SHAPE for x_rows < 0.
  */
-int dg_fp8_quantize_1x128_gather(const void *X, int x_dtype, int64_t ldx, int64_t x_rows,
-                                 const int32_t *src_rows,
-                                 void *Q, int64_t ldq,
-                                 float *S, int64_t s_stride_m, int64_t s_stride_kb,
-                                 int64_t M, int64_t K, void *stream);
+dg_status dg_fp8_quantize_1x128_gather(const void *X, int x_dtype, int64_t ldx, int64_t x_rows,
+                                       const int32_t *src_rows,
+                                       void *Q, int64_t ldq,
+                                       float *S, int64_t s_stride_m, int64_t s_stride_kb,
+                                       int64_t M, int64_t K, void *stream);
 
 /*
  * MoE routing into the contiguous layout that dg_fp8_grouped_gemm_contiguous
@@ -364,9 +427,9 @@ int dg_fp8_quantize_1x128_gather(const void *X, int x_dtype, int64_t ldx, int64_
  * M_cap >= dg_moe_contiguous_max_rows(T, G) (else DG_ERR_BAD_SHAPE); all
  * arrays 4-byte aligned and pairwise disjoint.
  */
-int dg_moe_route_contiguous(const int32_t *expert_of_token, int64_t T, int64_t G,
-                            int32_t *row_of_token, int32_t *expert_ids, int32_t *token_of_row,
-                            int32_t *layout, int64_t M_cap, void *stream);
+dg_status dg_moe_route_contiguous(const int32_t *expert_of_token, int64_t T, int64_t G,
+                                  int32_t *row_of_token, int32_t *expert_ids, int32_t *token_of_row,
+                                  int32_t *layout, int64_t M_cap, void *stream);
 
 /* Rows that always hold the padded layout of T tokens over G experts:
  * 128 * (ceil(T / 128) + min(G, T)). -1 for negative arguments. */
@@ -380,9 +443,9 @@ int64_t dg_moe_contiguous_max_rows(int64_t T, int64_t G);
  * Constraints: N % 8 == 0; D and out 16-byte aligned, ldd and ldo multiples
  * of 8; out disjoint from D and row_of_token.
  */
-int dg_moe_unpermute(const void *D, int64_t ldd, int64_t d_rows,
-                     const int32_t *row_of_token, int64_t T, int64_t N,
-                     void *out, int64_t ldo, void *stream);
+dg_status dg_moe_unpermute(const void *D, int64_t ldd, int64_t d_rows,
+                           const int32_t *row_of_token, int64_t T, int64_t N,
+                           void *out, int64_t ldo, void *stream);
 
 #ifdef __cplusplus
 }

@@ -18,13 +18,14 @@ DG_ERR_BAD_STRIDE, DG_ERR_UNSUPPORTED, DG_ERR_HIP, DG_ERR_ALIASING = 4, 5, 6, 7
 
 def declared_symbols():
     text = open(HEADER).read()
-    return sorted(set(re.findall(r"^\s*(?:int|int64_t|const char \*)\s*(dg_\w+)\s*\(", text, re.M)))
+    return sorted(set(re.findall(r"^\s*(?:int|int64_t|dg_status|const char \*)\s*(dg_\w+)\s*\(", text, re.M)))
 
 
 def test_header_declares_the_entry_points():
     syms = declared_symbols()
     for name in ("dg_fp8_gemm_nt", "dg_fp8_grouped_gemm_contiguous", "dg_fp8_grouped_gemm_masked",
-                 "dg_fp8_quantize_1x128",
+                 "dg_fp8_quantize_1x128", "dg_fp8_gemm_nt_ws", "dg_fp8_gemm_nt_workspace_bytes",
+                 "dg_fp8_grouped_gemm_contiguous_ws", "dg_fp8_grouped_gemm_contiguous_workspace_bytes",
                  "dg_abi_version", "dg_status_string", "dg_last_hip_error"):
         assert name in syms
 
@@ -38,7 +39,7 @@ def test_library_exports_every_declared_symbol():
 
 def test_version_and_status_strings():
     lib = _lib.load()
-    assert lib.dg_abi_version() == 1
+    assert lib.dg_abi_version() == 2
     for s in range(8):
         assert lib.dg_status_string(s)
     assert lib.dg_status_string(99) == b"unknown status"
@@ -85,6 +86,82 @@ def test_empty_problems_return_ok_without_device():
     assert nt(M=0) == DG_OK
     assert nt(N=0) == DG_OK
     assert nt(M=0, A=None, B=None, D=None) == DG_OK
+
+
+WS = 0x70000000
+
+
+def nt_ws(**kw):
+    args = dict(A=A, lda=512, sA=SA, sa_m=1, sa_kb=64, B=B, ldb=512, sB=SB, sb_nb=4, sb_kb=1,
+                D=D, ldd=256, M=64, N=256, K=512, ws=WS, ws_bytes=1 << 20, stream=None)
+    args.update(kw)
+    return _lib.load().dg_fp8_gemm_nt_ws(*args.values())
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(K=500, lda=512, ldb=512), DG_ERR_BAD_SHAPE),
+    (dict(A=None), DG_ERR_NULL_POINTER),
+    (dict(ws_bytes=-1), DG_ERR_BAD_SHAPE),
+    (dict(ws=WS + 8), DG_ERR_MISALIGNED),
+    (dict(ws=D), DG_ERR_ALIASING),                  # the workspace overlaps the output
+    (dict(ws=D - 4096, ws_bytes=8192), DG_ERR_ALIASING),
+    (dict(ws=A), DG_ERR_ALIASING),                  # ... or an input
+    (dict(ws=SB - 1024, ws_bytes=2048), DG_ERR_ALIASING),
+    (dict(D=A + 1024), DG_ERR_ALIASING),
+])
+def test_dense_ws_validation(kw, status):
+    assert nt_ws(**kw) == status
+
+
+def test_dense_ws_empty_and_unused_workspace():
+    assert nt_ws(M=0) == DG_OK
+    # a NULL workspace (or zero bytes) is the plain call: nothing to check about it
+    assert nt_ws(M=0, ws=None, ws_bytes=0) == DG_OK
+    assert nt_ws(M=0, ws=WS + 8, ws_bytes=0) == DG_OK
+
+
+def test_workspace_queries_reject_bad_shapes_on_the_host():
+    lib = _lib.load()
+    assert lib.dg_fp8_gemm_nt_workspace_bytes(64, 200, 512) == -DG_ERR_BAD_SHAPE
+    assert lib.dg_fp8_gemm_nt_workspace_bytes(64, 256, 500) == -DG_ERR_BAD_SHAPE
+    assert lib.dg_fp8_gemm_nt_workspace_bytes(-1, 256, 512) == -DG_ERR_BAD_SHAPE
+    assert lib.dg_fp8_gemm_nt_workspace_bytes(0, 256, 512) == 0
+    assert lib.dg_fp8_grouped_gemm_contiguous_workspace_bytes(200, 256, 512, 4) == -DG_ERR_BAD_SHAPE
+    assert lib.dg_fp8_grouped_gemm_contiguous_workspace_bytes(256, 256, 512, -1) == -DG_ERR_BAD_SHAPE
+    assert lib.dg_fp8_grouped_gemm_contiguous_workspace_bytes(0, 256, 512, 4) == 0
+    assert lib.dg_fp8_grouped_gemm_contiguous_workspace_bytes(256, 256, 512, 0) == 0
+
+
+def contig_ws(**kw):
+    args = dict(A=A, lda=512, sA=SA, sa_m=1, sa_kb=256, B=B, ldb=512, b_stride_g=256 * 512,
+                sB=SB, sb_g=8, sb_nb=4, sb_kb=1, ids=IDS, tok=None, layout=None, D=D, ldd=256, T=0,
+                M_total=256, N=256, K=512, G=4, ws=WS, ws_bytes=1 << 20, stream=None)
+    args.update(kw)
+    return _lib.load().dg_fp8_grouped_gemm_contiguous_ws(*args.values())
+
+
+TOK, LAYOUT = 0x80000000, 0x90000000
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(M_total=200), DG_ERR_BAD_SHAPE),
+    (dict(ids=None), DG_ERR_NULL_POINTER),
+    (dict(ws_bytes=-5), DG_ERR_BAD_SHAPE),
+    (dict(ws=WS + 4), DG_ERR_MISALIGNED),
+    (dict(ws=D + 1024), DG_ERR_ALIASING),
+    (dict(ws=IDS), DG_ERR_ALIASING),
+    (dict(ws=TOK, tok=TOK, T=100), DG_ERR_ALIASING),
+    (dict(ws=LAYOUT - 256, ws_bytes=512, layout=LAYOUT), DG_ERR_ALIASING),
+    (dict(tok=TOK + 2, T=100), DG_ERR_MISALIGNED),
+])
+def test_contiguous_ws_validation(kw, status):
+    assert contig_ws(**kw) == status
+
+
+def test_contiguous_ws_empty():
+    assert contig_ws(M_total=0) == DG_OK
+    assert contig_ws(G=0) == DG_OK
+    assert contig_ws(tok=TOK, T=0) == DG_OK     # token-order output with no rows
 
 
 def contig(**kw):

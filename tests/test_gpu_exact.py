@@ -216,44 +216,75 @@ def test_empty_problems(gpu_device):
     assert d.shape == (0, 128)
 
 
-def test_split_k_in_graph_capture(gpu_device):
-    # M=96, N=512 gives 4 tiles of 128x128, so the K blocks are split over
-    # work items and reduced by a second kernel. A capture on a stream that
-    # already ran the split replays bit-identically to the eager result (the
-    # slices are added in a fixed order); a capture on a fresh stream runs
-    # unsplit (nothing is allocated during a capture) and stays within
-    # tolerance of the oracle.
+def test_split_k_workspace_in_graph_capture(gpu_device):
+    # M=96, N=512 gives 4 tiles of 128x128, so with a workspace the K blocks
+    # are split over work items whose fp32 partials go to the caller's
+    # workspace, and a second kernel adds them in a fixed order. A captured
+    # graph keeps the workspace it was given. A later, larger split call on
+    # the same stream with its own workspace, and that workspace being freed,
+    # cannot disturb the graph (the library owns no memory): every replay
+    # equals the first eager result bit for bit.
     p = gen.make_dense(96, 512, 1024, 61, 62)
     ref = oracle.gemm_nt(p.a, p.sa_t.T, p.b, p.sb)
     a, sa, b, sb = dev(p.a), dev(p.sa_t).t(), dev(p.b), dev(p.sb)
+    need = ops.dg_fp8_gemm_nt_workspace_bytes(96, 512, 1024)
+    assert need == 8 * 96 * 512 * 4          # 8 slices of fp32 partials
+    ws1 = ops.workspace(need)
     s = torch.cuda.Stream()
     s.wait_stream(torch.cuda.current_stream())
     d = sentinel_bf16((96, 512))
     with torch.cuda.stream(s):
-        ops.dg_fp8_gemm_nt(a, sa, b, sb, d=d)
+        ops.dg_fp8_gemm_nt_ws(a, sa, b, sb, ws1, d=d)
     s.synchronize()
     eager = bits(d)
     assert_close(eager, ref, "split-K eager")
+    unsplit = run_dense(p.a, p.sa_t.T, p.b, p.sb)          # no workspace: one K loop per tile
+    assert_close(unsplit, ref, "unsplit")
+
     g = torch.cuda.CUDAGraph()
     d2 = sentinel_bf16((96, 512))
     with torch.cuda.graph(g, stream=s):
-        ops.dg_fp8_gemm_nt(a, sa, b, sb, d=d2)
+        ops.dg_fp8_gemm_nt_ws(a, sa, b, sb, ws1, d=d2)
+
+    q = gen.make_dense(200, 1024, 2048, 63, 64)           # a larger split call
+    qref = oracle.gemm_nt(q.a, q.sa_t.T, q.b, q.sb)
+    qa, qsa, qb, qsb = dev(q.a), dev(q.sa_t).t(), dev(q.b), dev(q.sb)
+    need2 = ops.dg_fp8_gemm_nt_workspace_bytes(200, 1024, 2048)
+    assert need2 > need
     for r in range(3):
+        ws2 = ops.workspace(need2)
+        with torch.cuda.stream(s):
+            dq = ops.dg_fp8_gemm_nt_ws(qa, qsa, qb, qsb, ws2, d=sentinel_bf16((200, 1024)))
+        s.synchronize()
+        assert_close(bits(dq), qref, "larger split call %d" % r)
+        del ws2, dq
+        torch.cuda.empty_cache()
         d2.fill_(0)
         torch.cuda.synchronize()
         with torch.cuda.stream(s):
             g.replay()
         s.synchronize()
         assert np.array_equal(bits(d2), eager), "replay %d" % r
-        ops.dg_fp8_gemm_nt(a, sa, b, sb, d=d)   # eager work between replays
+
+
+def test_split_k_partial_workspace(gpu_device):
+    # A workspace that holds fewer slices than the query asks for takes as
+    # many as it holds (here 3 of 8): a different grouping of the fp32 sums,
+    # so within tolerance of the oracle, and the same bits on every call.
+    p = gen.make_dense(96, 512, 1024, 65, 66)
+    ref = oracle.gemm_nt(p.a, p.sa_t.T, p.b, p.sb)
+    a, sa, b, sb = dev(p.a), dev(p.sa_t).t(), dev(p.b), dev(p.sb)
+    ws = ops.workspace(3 * 96 * 512 * 4 + 100)
+    first = None
+    for _ in range(5):
+        d = ops.dg_fp8_gemm_nt_ws(a, sa, b, sb, ws, d=sentinel_bf16((96, 512)))
         torch.cuda.synchronize()
-    fresh = torch.cuda.Stream()
-    fresh.wait_stream(torch.cuda.current_stream())
-    g2 = torch.cuda.CUDAGraph()
-    d3 = sentinel_bf16((96, 512))
-    with torch.cuda.graph(g2, stream=fresh):
-        ops.dg_fp8_gemm_nt(a, sa, b, sb, d=d3)
-    with torch.cuda.stream(fresh):
-        g2.replay()
-    fresh.synchronize()
-    assert_close(bits(d3), ref, "unsplit in capture")
+        got = bits(d)
+        if first is None:
+            first = got
+            assert_close(got, ref, "3 slices")
+        assert np.array_equal(got, first)
+    tiny = ops.workspace(96 * 512 * 4)                  # one slice: no split at all
+    d = ops.dg_fp8_gemm_nt_ws(a, sa, b, sb, tiny, d=sentinel_bf16((96, 512)))
+    torch.cuda.synchronize()
+    assert np.array_equal(bits(d), run_dense(p.a, p.sa_t.T, p.b, p.sb))

@@ -51,7 +51,9 @@ def test_dense_fuzz(gpu_device, seed):
     m_major = bool(rng.integers(0, 2))
     sa = dev(p.sa_t).t() if m_major else dev(np.ascontiguousarray(p.sa_t.T))
     d = padded(sentinel_bf16((M, N)), 8 * int(rng.integers(0, 3)))
-    if (fa, fb) == ("e4m3", "e4m3"):
+    if (fa, fb) == ("e4m3", "e4m3") and seed % 2:   # odd seeds: with a workspace (split-K)
+        ops.dg_fp8_gemm_nt_ws(a, sa, b, dev(p.sb), ops.workspace(ops.dg_fp8_gemm_nt_workspace_bytes(M, N, K)), d=d)
+    elif (fa, fb) == ("e4m3", "e4m3"):
         ops.dg_fp8_gemm_nt(a, sa, b, dev(p.sb), d=d)
     else:
         ops.dg_fp8_gemm_nt_fmt(a, sa, b, dev(p.sb), fa, fb, d=d)
@@ -71,7 +73,7 @@ def test_contiguous_fuzz(gpu_device, seed):
     probs = rng.dirichlet(np.ones(G) * 0.5)
     e = rng.choice(G, T, p=probs).astype(np.int32)
     c = gen.make_contiguous(G, T, N, K, 2100 + seed, 2200 + seed, 0, expert_of_token=e)
-    got = bits(_run_contiguous(c))
+    got = bits(_run_contiguous(c, ws=seed % 2 == 1))
     ref = oracle.grouped_contiguous(c.a, c.sa_t.T, c.b, c.sb, c.ids, np.full((c.M_total, N), SENTINEL, np.uint16))
     valid = c.ids >= 0
     assert np.all(got[~valid] == SENTINEL), "seed %d: padding rows written" % seed
@@ -79,9 +81,15 @@ def test_contiguous_fuzz(gpu_device, seed):
         assert_close(got[valid], ref[valid], "seed %d: G=%d T=%d N=%d K=%d" % (seed, G, T, N, K))
 
 
-def _run_contiguous(c):
+def _run_contiguous(c, ws=False):
+    """The plain call, or (ws) the call with the workspace its query asks for."""
     d = sentinel_bf16((c.M_total, c.N))
-    ops.dg_fp8_grouped_gemm_contiguous(dev(c.a), dev(c.sa_t).t(), dev(c.b), dev(c.sb), dev(c.ids), d=d)
+    args = (dev(c.a), dev(c.sa_t).t(), dev(c.b), dev(c.sb), dev(c.ids))
+    if ws:
+        w = ops.workspace(ops.dg_fp8_grouped_gemm_contiguous_workspace_bytes(c.M_total, c.N, c.K, c.G))
+        ops.dg_fp8_grouped_gemm_contiguous_ws(*args, w, d=d)
+    else:
+        ops.dg_fp8_grouped_gemm_contiguous(*args, d=d)
     torch.cuda.synchronize()
     return d
 
@@ -132,11 +140,13 @@ def test_contiguous_layout_fuzz(gpu_device, seed):
     ref = oracle.grouped_contiguous(c.a, c.sa_t.T, c.b, c.sb, c.ids, np.full((c.M_total, N), SENTINEL, np.uint16))
     valid = c.ids >= 0
     what = "seed %d: G=%d T=%d N=%d K=%d" % (seed, G, T, N, K)
+    # odd seeds give the call a workspace (tails split over K), even seeds none
+    w = ops.workspace(ops.dg_fp8_grouped_gemm_contiguous_workspace_bytes(c.M_total, N, K, G)) if seed % 2 else None
     if seed % 4 == 3:
         tok = c.token_of_row.astype(np.int32)
         out = sentinel_bf16((T, N))
-        ops.dg_fp8_grouped_gemm_contiguous_to_tokens(args[0], args[1], args[2], args[3], args[4], dev(tok), T,
-                                                     layout=dev(layout), out=out)
+        ops.dg_fp8_grouped_gemm_contiguous_ws(args[0], args[1], args[2], args[3], args[4], w,
+                                              token_of_row=dev(tok), T=T, layout=dev(layout), d=out)
         torch.cuda.synchronize()
         got = bits(out)
         assert_close(got[tok[valid]], ref[valid], what)
@@ -145,7 +155,10 @@ def test_contiguous_layout_fuzz(gpu_device, seed):
         assert np.all(got[~routed] == SENTINEL), what
         return
     d = sentinel_bf16((c.M_total, N))
-    ops.dg_fp8_grouped_gemm_contiguous_layout(*args, dev(layout), d=d)
+    if w is not None:
+        ops.dg_fp8_grouped_gemm_contiguous_ws(*args, w, layout=dev(layout), d=d)
+    else:
+        ops.dg_fp8_grouped_gemm_contiguous_layout(*args, dev(layout), d=d)
     torch.cuda.synchronize()
     got = bits(d)
     assert np.all(got[~valid] == SENTINEL), "%s: padding rows written" % what

@@ -139,15 +139,17 @@ def test_masked_full_size_graph_replay(gpu_device):
         assert_close(got[gs[sel], ms[sel], ns[sel]], ref[sel], "full-size replay")
 
 
-@pytest.mark.parametrize("K,use_layout", [(512, False), (2048, True)])
-def test_moe_step_graph_replay_with_changing_routing(gpu_device, K, use_layout):
+@pytest.mark.parametrize("K,use_layout,use_ws", [(512, False, False), (2048, True, True), (1024, False, True),
+                                                (1024, True, False)])
+def test_moe_step_graph_replay_with_changing_routing(gpu_device, K, use_layout, use_ws):
     """Routing, quantisation into the layout and the grouped GEMM to token
     order captured once; new routings and activations are copied into the
     captured buffers between replays. Nothing in the step reads sizes on the
-    host, so every replay must equal the eager chain bit for bit. With the
-    segment offsets at K 2048 the segments' last 128 rows are split over K:
-    one eager step on the capture stream first gives it the workspace, and the
-    slice count chosen on the device follows each routing."""
+    host, so every replay must equal the eager chain bit for bit. With a
+    caller workspace the segments' last 128 rows are split over K (K 1024 and
+    2048), and without the layout the segment offsets are derived into the
+    workspace on the device; the slice count chosen on the device follows
+    each routing."""
     T, G, N = 500, 6, 256
     b, sb = gen.make_grouped_rhs(G, N, K, 821)
     bd, sbd = dev(b), dev(sb)
@@ -161,6 +163,7 @@ def test_moe_step_graph_replay_with_changing_routing(gpu_device, K, use_layout):
     q = torch.empty((M_cap, K), dtype=torch.uint8, device="cuda")
     s = torch.empty((K // 128, M_cap), dtype=torch.float32, device="cuda").t()
     out = torch.empty((T, N), dtype=torch.bfloat16, device="cuda")
+    w = ops.workspace(ops.dg_fp8_grouped_gemm_contiguous_workspace_bytes(M_cap, N, K, G)) if use_ws else None
     lib = ops._lib.load()
 
     def step():
@@ -168,8 +171,12 @@ def test_moe_step_graph_replay_with_changing_routing(gpu_device, K, use_layout):
                                          layout.data_ptr(), M_cap, torch.cuda.current_stream().cuda_stream)
         assert st == 0
         ops.dg_fp8_quantize_1x128_gather(x, tok, q=q, s=s)
-        ops.dg_fp8_grouped_gemm_contiguous_to_tokens(q, s, bd, sbd, ids, tok, T, layout=layout if use_layout else None,
-                                                     out=out)
+        if use_ws:
+            ops.dg_fp8_grouped_gemm_contiguous_ws(q, s, bd, sbd, ids, w, token_of_row=tok, T=T,
+                                                  layout=layout if use_layout else None, d=out)
+        else:
+            ops.dg_fp8_grouped_gemm_contiguous_to_tokens(q, s, bd, sbd, ids, tok, T,
+                                                         layout=layout if use_layout else None, out=out)
 
     stream = torch.cuda.Stream()
     stream.wait_stream(torch.cuda.current_stream())

@@ -1,10 +1,12 @@
-"""Contiguous grouped GEMM tiled along the experts' segments (layout given).
+"""Contiguous grouped GEMM tiled along the experts' segments (layout given,
+or derived on the device into the caller's workspace).
 
 Rows in a segment's whole 256-row tiles go through the same per-element
 arithmetic as on the uniform grid, so they must equal the uniform-grid result
-bit for bit. A segment's last 128 rows (where its size is an odd multiple of
-128) may be split over K and summed slice by slice, which only regroups the
-fp32 additions: those rows are held to the oracle's tolerance. Every valid row
+bit for bit. With a workspace, a segment's last 128 rows (where its size is
+an odd multiple of 128) may be split over K and summed slice by slice, which
+only regroups the fp32 additions: those rows are held to the oracle's
+tolerance; without one they run unsplit and equal the grid too. Every valid row
 is held against the oracle, padding rows must stay untouched, and a layout
 that does not fit the rows must write nothing (and not fault).
 """
@@ -35,12 +37,18 @@ def tail_rows(layout, M):
     return mask
 
 
-def run_both(c, layout):
+def run_both(c, layout, ws=True):
+    """(uniform grid, segment tiles): the plain call, and the call given the
+    layout, with the workspace its query asks for (ws) or none."""
     args = (dev(c.a), dev(c.sa_t).t(), dev(c.b), dev(c.sb), dev(c.ids))
     d_grid = sentinel_bf16((c.M_total, c.N))
     ops.dg_fp8_grouped_gemm_contiguous(*args, d=d_grid)
     d_seg = sentinel_bf16((c.M_total, c.N))
-    ops.dg_fp8_grouped_gemm_contiguous_layout(*args, dev(layout), d=d_seg)
+    if ws:
+        w = ops.workspace(ops.dg_fp8_grouped_gemm_contiguous_workspace_bytes(c.M_total, c.N, c.K, c.G))
+        ops.dg_fp8_grouped_gemm_contiguous_ws(*args, w, layout=dev(layout), d=d_seg)
+    else:
+        ops.dg_fp8_grouped_gemm_contiguous_layout(*args, dev(layout), d=d_seg)
     torch.cuda.synchronize()
     return bits(d_grid), bits(d_seg)
 
@@ -55,7 +63,8 @@ def run_both(c, layout):
     (7, 1300, 384, 2048, 7),    # 4 slices
     (3, 900, 512, 4096, 8),     # 8 slices
 ])
-def test_segment_tiles_equal_grid_tiles_and_oracle(gpu_device, G, T, N, K, seed):
+@pytest.mark.parametrize("ws", [True, False])
+def test_segment_tiles_equal_grid_tiles_and_oracle(gpu_device, G, T, N, K, seed, ws):
     rng = np.random.default_rng(seed)
     p = rng.dirichlet(np.ones(G) * 0.7)
     if seed == 5:
@@ -65,8 +74,8 @@ def test_segment_tiles_equal_grid_tiles_and_oracle(gpu_device, G, T, N, K, seed)
     c = gen.make_contiguous(G, T, N, K, 700 + seed, 800 + seed, 0, expert_of_token=e)
     layout = layout_of(c.counts)
     assert layout[-1] == c.M_total
-    grid, seg = run_both(c, layout)
-    whole = ~tail_rows(layout, c.M_total)
+    grid, seg = run_both(c, layout, ws)
+    whole = ~tail_rows(layout, c.M_total) if ws else np.ones(c.M_total, bool)
     assert np.array_equal(seg[whole], grid[whole])
     valid = c.ids >= 0
     assert np.all(seg[~valid] == SENTINEL)
@@ -111,7 +120,8 @@ def test_to_tokens_with_layout(gpu_device):
     out0 = sentinel_bf16((T, N))
     ops.dg_fp8_grouped_gemm_contiguous_to_tokens(q, s, bd, sbd, ids, tok, T, out=out0)
     out1 = sentinel_bf16((T, N))
-    ops.dg_fp8_grouped_gemm_contiguous_to_tokens(q, s, bd, sbd, ids, tok, T, layout=layout, out=out1)
+    w = ops.workspace(ops.dg_fp8_grouped_gemm_contiguous_workspace_bytes(ids.shape[0], N, K, G))
+    ops.dg_fp8_grouped_gemm_contiguous_ws(q, s, bd, sbd, ids, w, token_of_row=tok, T=T, layout=layout, d=out1)
     torch.cuda.synchronize()
     lay, tk = layout.cpu().numpy(), tok.cpu().numpy()
     tails = tail_rows(lay, len(tk))
@@ -125,7 +135,8 @@ def test_to_tokens_with_layout(gpu_device):
 
 
 @pytest.mark.parametrize("kind", ["zeros", "past_the_rows", "negative"])
-def test_layout_that_does_not_fit_writes_nothing(gpu_device, kind):
+@pytest.mark.parametrize("ws", [True, False])
+def test_layout_that_does_not_fit_writes_nothing(gpu_device, kind, ws):
     G, T, N, K = 4, 300, 256, 256
     e = np.random.default_rng(6).choice(G, T).astype(np.int32)
     c = gen.make_contiguous(G, T, N, K, 951, 952, 0, expert_of_token=e)
@@ -135,7 +146,7 @@ def test_layout_that_does_not_fit_writes_nothing(gpu_device, kind):
         layout = (c.M_total + 128 * np.arange(G + 1)).astype(np.int32)
     else:
         layout = (-4096 + 256 * np.arange(G + 1)).astype(np.int32)
-    _, seg = run_both(c, layout)
+    _, seg = run_both(c, layout, ws)
     assert np.all(seg == SENTINEL)
 
 
@@ -158,11 +169,13 @@ def blocks_reordered(c, order_blocks):
 
 
 @pytest.mark.parametrize("case", ["descending", "interleaved", "padding_blocks"])
-def test_plain_call_any_block_order(gpu_device, case):
-    """The call given only the ids derives the segment offsets on the device
-    when the experts ascend (padding blocks anywhere allowed) and falls back to
-    the uniform grid otherwise; either way every valid row matches the oracle
-    and padding rows stay untouched."""
+@pytest.mark.parametrize("ws", [True, False])
+def test_plain_call_any_block_order(gpu_device, case, ws):
+    """The call given only the ids (and a workspace) derives the segment
+    offsets on the device when the experts ascend (padding blocks anywhere
+    allowed) and falls back to the uniform grid otherwise; without a
+    workspace it tiles the rows uniformly. Either way every valid row matches
+    the oracle and padding rows stay untouched."""
     G, T, N, K = 5, 900, 256, 1024
     e = np.random.default_rng(21).choice(G, T).astype(np.int32)
     c = gen.make_contiguous(G, T, N, K, 961, 962, 0, expert_of_token=e)
@@ -178,9 +191,14 @@ def test_plain_call_any_block_order(gpu_device, case):
     M = len(ids)
     args = (dev(a), dev(sa_t).t(), dev(c.b), dev(c.sb), dev(ids))
     d = sentinel_bf16((M, N))
-    ops.dg_fp8_grouped_gemm_contiguous(*args, d=d)
     out = sentinel_bf16((T, N))
-    ops.dg_fp8_grouped_gemm_contiguous_to_tokens(*args, dev(tok), T, out=out)
+    if ws:
+        w = ops.workspace(ops.dg_fp8_grouped_gemm_contiguous_workspace_bytes(M, N, K, G))
+        ops.dg_fp8_grouped_gemm_contiguous_ws(*args, w, d=d)
+        ops.dg_fp8_grouped_gemm_contiguous_ws(*args, w, token_of_row=dev(tok), T=T, d=out)
+    else:
+        ops.dg_fp8_grouped_gemm_contiguous(*args, d=d)
+        ops.dg_fp8_grouped_gemm_contiguous_to_tokens(*args, dev(tok), T, out=out)
     torch.cuda.synchronize()
     got = bits(d)
     ref = oracle.grouped_contiguous(a, sa_t.T, c.b, c.sb, ids, np.full((M, N), SENTINEL, np.uint16))
@@ -220,7 +238,8 @@ def plain_ids_case(kind):
 
 @pytest.mark.parametrize("kind", ["all_padding", "one_expert", "last_expert_only", "ids_out_of_range",
                                   "many_blocks", "no_split_k128"])
-def test_plain_call_edge_ids(gpu_device, kind):
+@pytest.mark.parametrize("ws", [True, False])
+def test_plain_call_edge_ids(gpu_device, kind, ws):
     ids, G, K = plain_ids_case(kind)
     M, N = len(ids), 256
     rng = np.random.Generator(np.random.PCG64(32))
@@ -228,7 +247,12 @@ def test_plain_call_edge_ids(gpu_device, kind):
     sa_t = np.ascontiguousarray(sa_t.T)
     b, sb = gen.make_grouped_rhs(G, N, K, 33)
     d = sentinel_bf16((M, N))
-    ops.dg_fp8_grouped_gemm_contiguous(dev(a), dev(sa_t).t(), dev(b), dev(sb), dev(ids), d=d)
+    args = (dev(a), dev(sa_t).t(), dev(b), dev(sb), dev(ids))
+    if ws:
+        w = ops.workspace(ops.dg_fp8_grouped_gemm_contiguous_workspace_bytes(M, N, K, G))
+        ops.dg_fp8_grouped_gemm_contiguous_ws(*args, w, d=d)
+    else:
+        ops.dg_fp8_grouped_gemm_contiguous(*args, d=d)
     torch.cuda.synchronize()
     got = bits(d)
     # a block's expert is its largest id in [0, G); only rows with that id are written
