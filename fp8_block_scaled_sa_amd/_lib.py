@@ -19,6 +19,8 @@ SIGNATURES = {
     "dg_fp8_gemm_nt_ws": (ctypes.c_int, [_p, _i64, _p, _i64, _i64, _p, _i64, _p, _i64, _i64,
                                          _p, _i64, _i64, _i64, _i64, _p, _i64, _p]),
     "dg_fp8_gemm_nt_workspace_bytes": (ctypes.c_int64, [_i64, _i64, _i64]),
+    "dg_fp8_gemm_nt_noalloc": (ctypes.c_int, [_p, _i64, _p, _i64, _i64, _p, _i64, _p, _i64, _i64,
+                                              _p, _i64, _i64, _i64, _i64, _p]),
     "dg_fp8_grouped_gemm_contiguous_ws": (ctypes.c_int, [_p, _i64, _p, _i64, _i64, _p, _i64, _i64,
                                                          _p, _i64, _i64, _i64, _p, _p, _p, _p, _i64, _i64,
                                                          _i64, _i64, _i64, _i64, _p, _i64, _p]),

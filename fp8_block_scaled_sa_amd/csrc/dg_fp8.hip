@@ -32,6 +32,50 @@ constexpr int kMaxDevices = 64;
 DeviceInfo g_devices[kMaxDevices];
 std::mutex g_devices_mu;
 
+// Scratch memory of dg_fp8_gemm_nt_noalloc, for callers that cannot
+// allocate: a fixed array in the library's code object. Each GPU the library
+// is loaded on holds its own copy until the process ends. Host code never
+// names the array itself (on the host its name is only a stand-in for the
+// device symbol): it takes each device's address once with
+// hipGetSymbolAddress, with that device current, and passes that address to
+// the kernels. 32 MiB holds the partial sums of every dense split-K launch on
+// a 256-CU device (at most 256 work items of 256x128 fp32 partial tiles).
+constexpr size_t kScratchBytes = (size_t)32 << 20;
+static __device__ __align__(256) uint8_t scratch[kScratchBytes];
+uint8_t *g_scratch_ptr[kMaxDevices];
+bool g_scratch_known[kMaxDevices];
+
+// The address of the current device's copy of `scratch`, resolved on the
+// first call on that device; nullptr (with the HIP error recorded) on failure.
+uint8_t *device_scratch(int &status)
+{
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) {
+        g_last_hip_error = (int)e;
+        status = DG_ERR_HIP;
+        return nullptr;
+    }
+    if (dev < 0 || dev >= kMaxDevices) {
+        status = DG_ERR_UNSUPPORTED;
+        return nullptr;
+    }
+    std::lock_guard<std::mutex> lk(g_devices_mu);
+    if (!g_scratch_known[dev]) {
+        void *ptr = nullptr;
+        e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || !ptr) {
+            g_last_hip_error = (int)e;
+            status = DG_ERR_HIP;
+            return nullptr;
+        }
+        g_scratch_ptr[dev] = (uint8_t *)ptr;
+        g_scratch_known[dev] = true;
+    }
+    status = DG_OK;
+    return g_scratch_ptr[dev];
+}
+
 int fail_hip(hipError_t e)
 {
     g_last_hip_error = (int)e;
@@ -882,7 +926,8 @@ const char *dg_status_string(dg_status status)
     case DG_ERR_BAD_STRIDE: return "bad stride (lda/ldb >= K, ldd >= N, non-negative, group strides cover a group)";
     case DG_ERR_UNSUPPORTED: return "unsupported device (gfx950 required) or size beyond int32";
     case DG_ERR_HIP: return "HIP runtime error (see dg_last_hip_error)";
-    case DG_ERR_ALIASING: return "output overlaps an input";
+    case DG_ERR_ALIASING: return "output (or workspace) overlaps an input or the output";
+    case DG_ERR_SCRATCH: return "the problem needs more scratch than the library's static buffer holds (use the _ws call)";
     default: return "unknown status";
     }
 }
@@ -975,6 +1020,39 @@ dg_status dg_fp8_grouped_gemm_contiguous_layout(const void *A, int64_t lda, cons
     return (dg_status)contiguous_impl(A, lda, sA, sa_stride_m, sa_stride_kb, B, ldb, b_stride_g, sB, sb_stride_g,
                            sb_stride_nb, sb_stride_kb, expert_ids, nullptr, D, ldd, M_total, M_total, N, K, G,
                            stream, 0, layout);
+}
+
+dg_status dg_fp8_gemm_nt_noalloc(const void *A, int64_t lda, const float *sA, int64_t sa_stride_m,
+                                 int64_t sa_stride_kb, const void *B, int64_t ldb, const float *sB,
+                                 int64_t sb_stride_nb, int64_t sb_stride_kb, void *D, int64_t ldd, int64_t M,
+                                 int64_t N, int64_t K, void *stream)
+{
+    dgk::Params p;
+    DeviceInfo dev;
+    int st = dense_setup(A, lda, sA, sa_stride_m, sa_stride_kb, B, ldb, sB, sb_stride_nb, sb_stride_kb, D, ldd,
+                         M, N, K, p, dev);
+    if (st != DG_OK)
+        return (dg_status)(st == kEmptyProblem ? DG_OK : st);
+    // What the fastest path takes, for these exact arguments (a dry run).
+    Ctx q;
+    q.cus = dev.cus;
+    q.dry = true;
+    dgk::Params pq = p;
+    if ((st = dense_dispatch(pq, q)) != DG_OK)
+        return (dg_status)st;
+    if (q.need > kScratchBytes)
+        return DG_ERR_SCRATCH;
+    uint8_t *ws = nullptr;
+    if (q.need > 0 && !(ws = device_scratch(st)))
+        return (dg_status)st;
+    // The split-K partial sums are written before they are read, so nothing
+    // in the array needs clearing between calls.
+    Ctx c;
+    c.cus = dev.cus;
+    c.stream = (hipStream_t)stream;
+    c.ws = ws;
+    c.ws_bytes = ws ? kScratchBytes : 0;
+    return (dg_status)dense_dispatch(p, c);
 }
 
 dg_status dg_fp8_grouped_gemm_contiguous_ws(const void *A, int64_t lda, const float *sA, int64_t sa_stride_m,

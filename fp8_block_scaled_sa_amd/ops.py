@@ -127,6 +127,25 @@ def dg_fp8_gemm_nt_ws(a, sa, b, sb, workspace, d=None, stream=None):
     return d
 
 
+def dg_fp8_gemm_nt_noalloc(a, sa, b, sb, d, stream=None):
+    """dg_fp8_gemm_nt_ws with the library's static scratch array as the
+    workspace: allocates nothing (d must be given)."""
+    _codes(a, "a", 2), _codes(b, "b", 2), _scales(sa, "sa", 2), _scales(sb, "sb", 2)
+    M, K = a.shape
+    N = b.shape[0]
+    if d.dtype != torch.bfloat16 or d.dim() != 2 or d.stride(-1) != 1 or tuple(d.shape) != (M, N):
+        raise TypeError("d must be a bfloat16 [M, N] tensor with contiguous rows")
+    if b.shape[1] != K:
+        raise ValueError("shape mismatch")
+    if tuple(sa.shape) != (M, K // BLOCK) or tuple(sb.shape) != (N // BLOCK, K // BLOCK):
+        raise ValueError("scale shape mismatch")
+    st = _lib.load().dg_fp8_gemm_nt_noalloc(_dev(a, "a"), a.stride(0), _dev(sa, "sa"), sa.stride(0), sa.stride(1),
+                                            _dev(b, "b"), b.stride(0), _dev(sb, "sb"), sb.stride(0), sb.stride(1),
+                                            _dev(d, "d"), d.stride(0), M, N, K, _stream(stream))
+    _check(st, "dg_fp8_gemm_nt_noalloc")
+    return d
+
+
 FORMATS = {"e4m3": 0, "e5m2": 1}   # DG_FP8_E4M3, DG_FP8_E5M2
 
 

@@ -80,7 +80,8 @@ typedef enum dg_status {
     DG_ERR_BAD_STRIDE = 4,   /* lda < K, ldb < K, ldd < N, negative or too small group stride */
     DG_ERR_UNSUPPORTED = 5,  /* current device is not gfx950, or a size exceeds int32 */
     DG_ERR_HIP = 6,          /* the HIP runtime failed (query or launch) */
-    DG_ERR_ALIASING = 7      /* D (or the workspace) overlaps an input or the output */
+    DG_ERR_ALIASING = 7,     /* D (or the workspace) overlaps an input or the output */
+    DG_ERR_SCRATCH = 8       /* dg_fp8_gemm_nt_noalloc: more scratch needed than its static buffer holds */
 } dg_status;
 
 /* Version of this ABI (DG_ABI_VERSION). */
@@ -141,6 +142,29 @@ dg_status dg_fp8_gemm_nt_ws(const void *A, int64_t lda,
                             void *D, int64_t ldd,
                             int64_t M, int64_t N, int64_t K,
                             void *workspace, int64_t workspace_bytes, void *stream);
+
+/*
+ * dg_fp8_gemm_nt_ws for callers that cannot allocate device memory (code
+ * under graph capture, tight serving loops, harnesses that forbid it): the
+ * split-K partial sums go to a 32 MiB array inside the library's code object
+ * instead of a caller workspace. Each GPU the library runs on holds its own
+ * copy of the array until the process ends; the call allocates nothing and
+ * calls no allocating routine. Results are bit-identical to dg_fp8_gemm_nt_ws
+ * given a workspace of dg_fp8_gemm_nt_workspace_bytes bytes.
+ * Limit: a problem whose split-K path needs more than 32 MiB returns
+ * DG_ERR_SCRATCH before anything is enqueued (no dense shape does on a
+ * 256-CU MI355X: at most 256 partial tiles of 256x128 fp32).
+ * Every call on one GPU shares that GPU's array: calls whose kernels may
+ * overlap in time (different streams without ordering, several host threads)
+ * race on it and must not be issued; calls on one stream are ordered and
+ * safe. Other arguments and errors as dg_fp8_gemm_nt.
+ */
+dg_status dg_fp8_gemm_nt_noalloc(const void *A, int64_t lda,
+                                 const float *sA, int64_t sa_stride_m, int64_t sa_stride_kb,
+                                 const void *B, int64_t ldb,
+                                 const float *sB, int64_t sb_stride_nb, int64_t sb_stride_kb,
+                                 void *D, int64_t ldd,
+                                 int64_t M, int64_t N, int64_t K, void *stream);
 
 /*
  * Workspace bytes the fastest path of dg_fp8_gemm_nt_ws takes for this shape
