@@ -65,6 +65,7 @@ BOUNDS = {
     "moe_contiguous_g8_t8192_seg": ("mfma", None),
     "moe_masked_g32_m256": ("hbm", 0.6),
 }
+NO_BENCH_ORACLE = {"square_4096_e4m3xe5m2"}
 CHUNK = 10          # launches per timed graph replay of the distribution
 MIN_LAUNCHES = 100  # launches timed per workload for the distribution, at least
 
@@ -263,6 +264,9 @@ def parity(got, ref):
             "exact": round(rep["exact"] / n, 6), "max_err_over_tol": round(rep["max_err_over_tol"], 4)}
 
 
+DISTRIBUTION = True
+
+
 def bench_gemm(name, steps, warmup, check, threads):
     """One GEMM workload: graph-timed mean over `steps` launches, the launch
     distribution, roofline, parity and the oracle's time on the same problem."""
@@ -278,12 +282,17 @@ def bench_gemm(name, steps, warmup, check, threads):
     torch.cuda.synchronize()
     per, wall = graph_time(run, steps, 0)
     mean_us = per[0]
-    dist = distribution(run, 2)
+    dist = distribution(run, 2) if DISTRIBUTION else None
     r = {"kernel_avg_us": round(mean_us, 3), "wall_ms_per_step": round(wall / steps * 1e3, 6),
          "us": dist, "tflops": round(flops / mean_us / 1e6, 2), "gbs": round(byts / mean_us / 1e3, 1),
          "algorithmic_flops": flops, "algorithmic_bytes": byts, "rows": rows, "operand_copies": len(run.copies),
          "roofline": roofline(name, flops, byts, mean_us), "traffic": load_traffic(name)}
-    if check:
+    # The e5m2 oracle sums each block exactly in 128-bit integers, ~50x slower
+    # than the e4m3 one: the whole 4096^3 problem takes minutes, so that
+    # variant's whole-output parity lives in the test suite only.
+    if check and name in NO_BENCH_ORACLE:
+        r["parity"] = "not checked here: tests/test_gpu_parity.py compares every element"
+    elif check:
         run.d.view(torch.int16).fill_(SENTINEL)
         run(0)
         torch.cuda.synchronize()
@@ -323,7 +332,8 @@ def time_quant(name, steps, warmup, check, threads):
     per, _ = graph_time(run, steps, warmup)
     us = per[0]
     byts = M * K * xc.element_size() + M * K + M * (K // 128) * 4
-    r = {"kernel_avg_us": round(us, 2), "us": distribution(run, 2), "gbs": round(byts / us / 1e3, 1),
+    r = {"kernel_avg_us": round(us, 2), "us": distribution(run, 2) if DISTRIBUTION else None,
+         "gbs": round(byts / us / 1e3, 1),
          "roofline": {"bound": "hbm", "achieved": round(byts / us / 1e3, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                       "frac": round(byts / us / 1e3 / HBM_PEAK_GBS, 4), "target_frac": None},
          "algorithmic_bytes": byts, "traffic": load_traffic(name, QUANT_SOURCES), "input_copies": n}
@@ -410,7 +420,8 @@ def time_moe_layer(steps, warmup):
               for k, f in (("route", route), ("quantize_gather", quant), ("grouped_gemm_to_tokens", gemm_to_tokens),
                            ("grouped_gemm", gemm), ("unpermute", unperm))}
     flops = 2 * T * N * K
-    r = {"us_per_step": round(total, 2), "us_per_step_unfused": round(unfused, 2), "us": distribution(step, 2),
+    r = {"us_per_step": round(total, 2), "us_per_step_unfused": round(unfused, 2),
+         "us": distribution(step, 2) if DISTRIBUTION else None,
          "tflops": round(flops / total / 1e6, 1), "stages_us": stages,
          "roofline": {"bound": "mfma", "achieved": round(flops / total / 1e6, 1), "peak": FP8_PEAK_TFLOPS,
                       "unit": "TFLOP/s", "frac": round(flops / total / 1e6 / FP8_PEAK_TFLOPS, 4), "target_frac": None},
@@ -454,6 +465,8 @@ def main():
                     help="comma-separated extra workloads to time, 'all' or 'none'")
     ap.add_argument("--no-cpu-baseline", action="store_true",
                     help="skip the oracle (parity verdicts and CPU timings), e.g. under a profiler")
+    ap.add_argument("--no-distribution", action="store_true",
+                    help="skip the per-launch timing distribution (fewer launches under a profiler)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
@@ -465,6 +478,8 @@ def main():
     assert torch.cuda.is_available(), "needs a GPU"
     check = not args.no_cpu_baseline
     threads = host_threads()
+    global DISTRIBUTION
+    DISTRIBUTION = not args.no_distribution
 
     head, p = bench_gemm(args.workload, args.steps, args.warmup, check, threads)
     kind = gen.CONFIGS[args.workload]["kind"]

@@ -263,11 +263,19 @@ __device__ __forceinline__ void tile_coords(int t, int tiles_m, int tiles_n, int
 // columns must lie in one 128-wide sB block), WAVES_M x WAVES_N waves, each
 // owning a (BM/WAVES_M) x (BN/WAVES_N) block of 16x16 sub-tiles. STAGES LDS
 // buffers, each holding one K block of the A tile, the B tile and sA.
-template <int BM, int BN, int WAVES_M, int WAVES_N, int STAGES, int GROUP_M, bool STREAM_B = false>
+template <int BM, int BN, int WAVES_M, int WAVES_N, int STAGES, int GROUP_M, bool STREAM_B = false,
+          bool EARLY_B = false>
 struct TileCfg {
     // B rows are read once per launch (each group's B feeds a single M tile):
     // load them non-temporally.
     static constexpr bool kStreamB = STREAM_B;
+    // Two stages only: every wave holds all of its B fragments of a K block in
+    // registers from row 0 on, so the B half of a stage is free once every
+    // wave is past row 0. A second barrier there lets the copy of B for block
+    // k + 2 start during block k, about one block earlier than the A copy of
+    // the same stage: B, the operand streamed from HBM in the grouped
+    // layouts, gets about two blocks of lead instead of one.
+    static constexpr bool kEarlyB = EARLY_B;
     static constexpr int kBM = BM, kBN = BN, kStages = STAGES, kGroupM = GROUP_M;
     static constexpr int kWavesM = WAVES_M, kWavesN = WAVES_N;
     static constexpr int kWaves = WAVES_M * WAVES_N;
@@ -298,6 +306,7 @@ struct TileCfg {
     static_assert(BN % 128 == 0, "tile columns cover whole sB blocks");
     static_assert(STAGES >= 2 && STAGES <= 4, "pipeline depth (the K loop is unrolled by at most 4)");
     static_assert(kSmemBytes <= 160 * 1024, "LDS");
+    static_assert(!EARLY_B || (STAGES == 2 && kDmaUpper), "early B copies: two stages, copies on the upper waves");
     static_assert((kSegPerWave + 2) * (STAGES - 2) < 64, "vmcnt range");
 };
 
@@ -524,12 +533,13 @@ __global__ void __launch_bounds__(C::kThreads, 1) tile_kernel(Params p)
         const uint32_t vb0 = voff_b + (uint32_t)(w_dma * 8 * p.ldb);
         const uint32_t step_a = (uint32_t)(C::kDmaWaves * 8 * p.lda);
         const uint32_t step_b = (uint32_t)(C::kDmaWaves * 8 * p.ldb);
-        auto issue = [&](int kb, int stage) {
+        const bool issues_ops = !(C::kDmaUpper && wave < C::kWaves / 2);  // the lower half issues no operand copies
+        // The copies of one K block into `stage`: the A tile (with sA and sB),
+        // then the B tile.
+        auto issue_a = [&](int kb, int stage) {
             const uint32_t sbase = smem_base + stage * C::kStageBytes;
             const uint32_t seg0 = sbase + w_dma * 1024;  // this wave's first segment
-            if (C::kDmaUpper && wave < C::kWaves / 2) {
-                // the lower half of the waves issues no operand copies
-            } else {
+            if (issues_ops) {
                 uint32_t o = va0;
 #pragma unroll
                 for (int q = 0; q < C::kDmaQA; ++q) {
@@ -537,7 +547,16 @@ __global__ void __launch_bounds__(C::kThreads, 1) tile_kernel(Params p)
                     if (q + 1 < C::kDmaQA)
                         o = add_in_place(o, step_a);
                 }
-                o = vb0;
+            }
+            if (loads_sa)
+                dma_b32(sAb + (int64_t)kb * p.sa_kb, voff_sa, sbase + C::kOffSa + wave * 256);
+            if (loads_sb)
+                dma_b32(sBb + (int64_t)kb * p.sb_kb, voff_sb, sbase + C::kOffSb);
+        };
+        auto issue_b = [&](int kb, int stage) {
+            const uint32_t seg0 = smem_base + stage * C::kStageBytes + w_dma * 1024;
+            if (issues_ops) {
+                uint32_t o = vb0;
 #pragma unroll
                 for (int q = C::kDmaQA; q < C::kDmaQ; ++q) {
                     if (C::kStreamB)
@@ -548,6 +567,24 @@ __global__ void __launch_bounds__(C::kThreads, 1) tile_kernel(Params p)
                         o = add_in_place(o, step_b);
                 }
             }
+        };
+        auto issue = [&](int kb, int stage) {
+            if (C::kEarlyB) {   // only the A copy here; B was issued a block earlier
+                issue_a(kb, stage);
+                return;
+            }
+            if (issues_ops) {
+                const uint32_t seg0 = smem_base + stage * C::kStageBytes + w_dma * 1024;
+                uint32_t o = va0;
+#pragma unroll
+                for (int q = 0; q < C::kDmaQA; ++q) {
+                    dma_buf_b128(rsrc_a, o, kb * 128, seg0 + q * C::kDmaWaves * 1024);
+                    if (q + 1 < C::kDmaQA)
+                        o = add_in_place(o, step_a);
+                }
+                issue_b(kb, stage);
+            }
+            const uint32_t sbase = smem_base + stage * C::kStageBytes;
             if (loads_sa)
                 dma_b32(sAb + (int64_t)kb * p.sa_kb, voff_sa, sbase + C::kOffSa + wave * 256);
             if (loads_sb)
@@ -584,7 +621,7 @@ __global__ void __launch_bounds__(C::kThreads, 1) tile_kernel(Params p)
         bool wave_active = wm0 < rows;
         if (L == kContiguous && npass == 2)
             wave_active = wave_active && ((wm0 < 128) == (pass == 0));
-        auto compute = [&](auto stage_c) {
+        auto compute = [&](auto stage_c, auto &&after_row0) {
             constexpr int st = decltype(stage_c)::value;
             const uint8_t *As = smem + st * C::kStageBytes;
             const uint8_t *Bs = As + C::kOffB;
@@ -633,32 +670,68 @@ __global__ void __launch_bounds__(C::kThreads, 1) tile_kernel(Params p)
                 }
                 __builtin_amdgcn_sched_barrier(0);
                 part_sc = sa * sb;
+                if (i == 0)
+                    after_row0();
             }
         };
 
         // One pipeline step for K block kb held in stage st = kb % S.
         auto step = [&](auto stage_c, int kb) {
             constexpr int st = decltype(stage_c)::value;
-            // Stage kb has landed once at most (S-2) later stages are in flight.
-            if (kb + S - 2 < nk)
-                wait_stage<SEGW, S - 2>(per_stage);
-            else
-                wait_vmcnt<0>();
+            if constexpr (C::kEarlyB) {
+                // In flight after this block's A copy: the B copy of block
+                // kb + 1 (this wave's B segments), if there is one.
+                if (issues_ops && kb + 1 < nk)
+                    wait_vmcnt<C::kDmaQ - C::kDmaQA>();
+                else
+                    wait_vmcnt<0>();
+            } else {
+                // Stage kb has landed once at most (S-2) later stages are in flight.
+                if (kb + S - 2 < nk)
+                    wait_stage<SEGW, S - 2>(per_stage);
+                else
+                    wait_vmcnt<0>();
+            }
+            // this wave's reads of the previous block have returned, so the
+            // stage they read may be overwritten once every wave is here
+            asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
             wg_barrier();  // every wave's DMA for kb is visible; stage (kb-1)%S is free
             if (kb + S - 1 < nk)
                 issue(kb + S - 1, (st + S - 1) % S);
+            // Early B: once every wave holds its B fragments of block kb (row 0
+            // has issued its MFMAs, so they have been read), B of block kb + 2
+            // goes into this stage's B half.
+            auto early_b = [&]() {
+                if constexpr (C::kEarlyB) {
+                    // this wave's B fragment reads have returned
+                    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+                    wg_barrier();
+                    if (kb + 2 < nk)
+                        issue_b(kb + 2, st);
+                }
+            };
             if (wave_active)
-                compute(stage_c);
+                compute(stage_c, early_b);
+            else
+                early_b();
         };
 
         // The previous tile's stores have completed (the vmcnt bookkeeping
         // counts only this tile's DMA) and its LDS reads are done.
         wait_vmcnt<0>();
         wg_barrier();
+        if constexpr (C::kEarlyB) {
+            // block 0 whole, and B of block 1 (A of block 1 follows in step 0)
+            issue_a(0, 0);
+            issue_b(0, 0);
+            if (1 < nk)
+                issue_b(1, 1);
+        } else {
 #pragma unroll
-        for (int s = 0; s < S - 1; ++s)
-            if (s < nk)
-                issue(s, s);
+            for (int s = 0; s < S - 1; ++s)
+                if (s < nk)
+                    issue(s, s);
+        }
         for (int kb0 = 0; kb0 < nk; kb0 += S) {
             step(std::integral_constant<int, 0>{}, kb0);
             if (kb0 + 1 < nk)
