@@ -675,7 +675,6 @@ int dense_setup(const void *A, int64_t lda, const float *sA, int64_t sa_stride_m
 int contiguous_dispatch(dgk::Params &p, Ctx &c, bool scatter, int fmt)
 {
     const int64_t N = p.N, G = p.G;
-    int st = DG_OK;
     const int ov = tile_override();  // 24: no derivation; 2, 3, 4 force the uniform grid's tile shape
     if (p.layout) {
         const bool wide = N % 256 == 0;
@@ -688,14 +687,14 @@ int contiguous_dispatch(dgk::Params &p, Ctx &c, bool scatter, int fmt)
     }
     // Only the ids given: with workspace for the offsets, derive the segment
     // offsets on the device and tile along them (e4m3, 256-wide tiles, at
-    // most 4096 blocks of 128 rows). The uniform-grid launch below then runs
-    // only if the ids' experts were not in ascending order, which the
-    // derivation flags. Up to 128 experts: at 8192 tokens, N 4096, K 7168 this
-    // measured 9-31% faster than the uniform grid for 8-64 experts and 2%
-    // faster at 128; at 256 (every segment one 128-row block) it was 2%
-    // slower, the per-tile segment search then outweighing the saved
-    // two-expert passes. Workspace: the offsets first (G + 2 int32), then the
-    // split tails' partial sums.
+    // most 4096 blocks of 128 rows). If the ids' experts are not in ascending
+    // order, the derivation flags it and the segment launch of whole tiles
+    // covers the rows on the uniform grid instead. Up to 128 experts: at 8192
+    // tokens, N 4096, K 7168 this measured 9-31% faster than the uniform grid
+    // for 8-64 experts and 2% faster at 128; at 256 (every segment one
+    // 128-row block) it was 2% slower, the per-tile segment search then
+    // outweighing the saved two-expert passes. Workspace: the offsets first
+    // (G + 2 int32), then the split tails' partial sums.
     if (!fmt && N % 256 == 0 && G <= kDeriveMaxExperts && p.M / 128 <= dgm::kDeriveMaxBlocks && ov != 24 &&
         ov != 2 && ov != 3 && ov != 4) {
         const size_t aux_bytes = ws_round((size_t)(G + 2) * sizeof(int32_t));
@@ -710,13 +709,10 @@ int contiguous_dispatch(dgk::Params &p, Ctx &c, bool scatter, int fmt)
             }
             dgk::Params q = p;
             q.layout = aux;
-            st = scatter ? launch_contiguous_seg<CfgBig, CfgTail, true>(q, c, aux_bytes)
+            q.gate = aux ? aux + G + 1 : nullptr;
+            return scatter ? launch_contiguous_seg<CfgBig, CfgTail, true>(q, c, aux_bytes)
                  : ov == 27 ? launch_contiguous_seg<CfgBig, CfgTail, false>(q, c, aux_bytes)
                             : launch_contiguous_seg<CfgBigE, CfgTail, false>(q, c, aux_bytes);
-            if (st != DG_OK)
-                return st;
-            if (aux)
-                p.gate = aux + G + 1;
         }
     }
     if (scatter) {

@@ -384,8 +384,28 @@ __global__ void __launch_bounds__(C::kThreads, 1) tile_kernel(Params p)
     // of one expert only: first the whole 256-row tiles of every segment
     // (expert by expert), then each segment's last 128 rows where its size is
     // an odd multiple of 128. full / half: how many of each.
+    // A segment launch of whole tiles whose offsets were derived on the device
+    // covers the rows block by block instead when the derivation found the
+    // experts out of order (*gate != 0; the offsets are then all zero): every
+    // aligned 128-row block is a tile of its own, half of the workgroup's
+    // rows, with the block's expert taken from the ids as on the uniform grid.
+    const bool by_block = SEG && p.seg_mode != 2 && p.gate && *p.gate != 0;
+    const int num_tiles = by_block ? (p.M >> 7) * p.tiles_n : p.num_tiles;
+    // Expert of an aligned 128-row block: the largest valid id in it (-1 if it
+    // holds padding only or lies past M_total).
+    auto block_expert = [&](int blk0) {
+        if (blk0 >= p.M)
+            return -1;
+        int e0 = p.ids[blk0 + lane], e1 = p.ids[blk0 + 64 + lane];
+        e0 = (e0 >= 0 && e0 < p.G) ? e0 : -1;
+        e1 = (e1 >= 0 && e1 < p.G) ? e1 : -1;
+        int e = max(e0, e1);
+        for (int o = 32; o > 0; o >>= 1)
+            e = max(e, __shfl_xor(e, o));
+        return __builtin_amdgcn_readfirstlane(e);
+    };
     int seg_full = 0, seg_half = 0;
-    if constexpr (SEG) {
+    if (SEG && !by_block) {
         for (int e = 0; e < p.G; ++e) {
             const int sz = p.layout[e + 1] - p.layout[e];
             if (sz > 0) {
@@ -399,14 +419,23 @@ __global__ void __launch_bounds__(C::kThreads, 1) tile_kernel(Params p)
     const int ks = L == kDense ? max(p.ksplit, 1)
                                : (SEG && p.seg_mode == 2 ? tail_split(seg_half * p.tiles_n, nk_all, p.ksplit, p.tail_slots) : 1);
 
-    for (int t = xcd_local_id(blockIdx.x, gridDim.x); t < p.num_tiles; t += gridDim.x) {
+    for (int t = xcd_local_id(blockIdx.x, gridDim.x); t < num_tiles; t += gridDim.x) {
         int g = 0, mt, nt;
         // split-K: work item t is K slice t % ks of tile t / ks
         const int slice = t % ks;
         const int kb_lo = (int)((int64_t)slice * nk_all / ks);
         const int nk = (int)((int64_t)(slice + 1) * nk_all / ks) - kb_lo;  // K blocks of this item
         int seg_m0 = 0, seg_rows = 0, seg_e = 0, seg_h = 0;
-        if constexpr (SEG) {
+        if (SEG && by_block) {
+            mt = 0;
+            int blk;
+            tile_coords(t, p.M >> 7, p.tiles_n, C::kGroupM, blk, nt);
+            seg_m0 = 128 * blk;
+            seg_rows = 128;
+            seg_e = block_expert(seg_m0);
+            if (seg_e < 0)
+                continue;  // padding only (uniform over the workgroup)
+        } else if (SEG) {
             mt = 0;
             // tails-only mode numbers its items from 0 after the whole tiles
             const int ts = p.seg_mode == 2 ? seg_full * p.tiles_n + t / ks : t;
@@ -468,19 +497,6 @@ __global__ void __launch_bounds__(C::kThreads, 1) tile_kernel(Params p)
             ex0 = ex1 = seg_e;
             rows = min(seg_rows, p.M - m0);
         } else {
-            // Expert of an aligned 128-row block: the largest valid id in it
-            // (-1 if it holds padding only or lies past M_total).
-            auto block_expert = [&](int blk0) {
-                if (blk0 >= p.M)
-                    return -1;
-                int e0 = p.ids[blk0 + lane], e1 = p.ids[blk0 + 64 + lane];
-                e0 = (e0 >= 0 && e0 < p.G) ? e0 : -1;
-                e1 = (e1 >= 0 && e1 < p.G) ? e1 : -1;
-                int e = max(e0, e1);
-                for (int o = 32; o > 0; o >>= 1)
-                    e = max(e, __shfl_xor(e, o));
-                return __builtin_amdgcn_readfirstlane(e);
-            };
             ex0 = block_expert(m0 & ~127);
             ex1 = BM > 128 ? block_expert(m0 + 128) : ex0;
             if (ex0 < 0 && ex1 < 0)
@@ -752,7 +768,10 @@ __global__ void __launch_bounds__(C::kThreads, 1) tile_kernel(Params p)
                 return m < p.M;
             if (L == kMasked)
                 return m < limit;
-            return m < p.M && p.ids[m] == expert;
+            // a segment tile covers seg_rows rows (128 for a segment's tail
+            // or a block on its own): the rows after them belong to another
+            // tile, possibly of the same expert
+            return m < p.M && (!SEG || m - m0 < seg_rows) && p.ids[m] == expert;
         };
         if (to_ws) {
 #pragma unroll

@@ -226,6 +226,8 @@ struct DeriveParams {
     int32_t *use_grid;   // [1]
 };
 
+constexpr int kDeriveBatch = 8;  // 128-row blocks per wave and round of id loads
+
 __global__ __launch_bounds__(kRouteThreads) void derive_layout_kernel(DeriveParams p)
 {
     __shared__ int bexp[kDeriveMaxBlocks];  // block experts, then their prefix maximum
@@ -233,15 +235,27 @@ __global__ __launch_bounds__(kRouteThreads) void derive_layout_kernel(DerivePara
     const int lane = threadIdx.x & 63;
     const int w = threadIdx.x >> 6;
     const int nb = p.M >> 7;
-    for (int b = w; b < nb; b += kRouteWaves) {
-        int e0 = p.ids[128 * b + lane], e1 = p.ids[128 * b + 64 + lane];
-        e0 = (e0 >= 0 && e0 < p.G) ? e0 : -1;
-        e1 = (e1 >= 0 && e1 < p.G) ? e1 : -1;
-        int e = max(e0, e1);
-        for (int o = 32; o > 0; o >>= 1)
-            e = max(e, __shfl_xor(e, o));
-        if (lane == 0)
-            bexp[b] = e;
+    // Each wave takes kDeriveBatch consecutive blocks at a time and issues all
+    // of their id loads before the first reduction, so the loads' latencies
+    // overlap (blocks past the end re-read the last block and are dropped).
+    for (int b0 = w * kDeriveBatch; b0 < nb; b0 += kRouteWaves * kDeriveBatch) {
+        int e0[kDeriveBatch], e1[kDeriveBatch];
+#pragma unroll
+        for (int j = 0; j < kDeriveBatch; ++j) {
+            const int b = min(b0 + j, nb - 1);
+            e0[j] = p.ids[128 * b + lane];
+            e1[j] = p.ids[128 * b + 64 + lane];
+        }
+#pragma unroll
+        for (int j = 0; j < kDeriveBatch; ++j) {
+            const int a0 = (e0[j] >= 0 && e0[j] < p.G) ? e0[j] : -1;
+            const int a1 = (e1[j] >= 0 && e1[j] < p.G) ? e1[j] : -1;
+            int e = max(a0, a1);
+            for (int o = 32; o > 0; o >>= 1)
+                e = max(e, __shfl_xor(e, o));
+            if (lane == 0 && b0 + j < nb)
+                bexp[b0 + j] = e;
+        }
     }
     __syncthreads();
     if (w == 0) {
