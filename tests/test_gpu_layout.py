@@ -270,3 +270,34 @@ def test_plain_call_edge_ids(gpu_device, kind, ws):
     ref, _, produced = oracle.grouped_contiguous_points(a, sa_t.T, b, sb, ids, rr, ns)
     assert produced.all()
     assert_close(got[rr, ns], ref, "plain call edge case %s" % kind)
+
+
+@pytest.mark.parametrize("G,N", [(64, 4096), (128, 4096), (64, 256), (128, 256)])
+@pytest.mark.parametrize("ws", [True, False])
+def test_plain_call_many_experts(gpu_device, G, N, ws):
+    """8192 tokens over 64 or 128 experts, the plain call and the token-order
+    call. With a workspace the offsets are derived on the device; at N 4096
+    the experts' tails fill two rounds on their own, so they are not split
+    over K (many 128-row tails on 256-row tiles), at N 256 they are split.
+    Every routed row against the oracle, padding rows untouched."""
+    T, K = 8192, 512
+    e = np.random.Generator(np.random.PCG64(980 + G)).choice(G, T).astype(np.int32)
+    c = gen.make_contiguous(G, T, N, K, 981, 982, 0, expert_of_token=e)
+    args = (dev(c.a), dev(c.sa_t).t(), dev(c.b), dev(c.sb), dev(c.ids))
+    tok = c.token_of_row.astype(np.int32)
+    d = sentinel_bf16((c.M_total, N))
+    out = sentinel_bf16((T, N))
+    if ws:
+        w = ops.workspace(ops.dg_fp8_grouped_gemm_contiguous_workspace_bytes(c.M_total, N, K, G))
+        ops.dg_fp8_grouped_gemm_contiguous_ws(*args, w, d=d)
+        ops.dg_fp8_grouped_gemm_contiguous_ws(*args, w, token_of_row=dev(tok), T=T, d=out)
+    else:
+        ops.dg_fp8_grouped_gemm_contiguous(*args, d=d)
+        ops.dg_fp8_grouped_gemm_contiguous_to_tokens(*args, dev(tok), T, out=out)
+    torch.cuda.synchronize()
+    got, got_tok = bits(d), bits(out)
+    ref = oracle.grouped_contiguous(c.a, c.sa_t.T, c.b, c.sb, c.ids, np.full((c.M_total, N), SENTINEL, np.uint16))
+    valid = c.ids >= 0
+    assert np.all(got[~valid] == SENTINEL)
+    assert_close(got[valid], ref[valid], "G=%d N=%d ws=%s" % (G, N, ws))
+    assert np.array_equal(got_tok[tok[valid]], got[valid]), "token order equals the plain call's rows"
