@@ -226,8 +226,6 @@ struct DeriveParams {
     int32_t *use_grid;   // [1]
 };
 
-constexpr int kDeriveBatch = 8;  // 128-row blocks per wave and round of id loads
-
 __global__ __launch_bounds__(kRouteThreads) void derive_layout_kernel(DeriveParams p)
 {
     __shared__ int bexp[kDeriveMaxBlocks];  // block experts, then their prefix maximum
@@ -235,27 +233,37 @@ __global__ __launch_bounds__(kRouteThreads) void derive_layout_kernel(DerivePara
     const int lane = threadIdx.x & 63;
     const int w = threadIdx.x >> 6;
     const int nb = p.M >> 7;
-    // Each wave takes kDeriveBatch consecutive blocks at a time and issues all
-    // of their id loads before the first reduction, so the loads' latencies
-    // overlap (blocks past the end re-read the last block and are dropped).
-    for (int b0 = w * kDeriveBatch; b0 < nb; b0 += kRouteWaves * kDeriveBatch) {
-        int e0[kDeriveBatch], e1[kDeriveBatch];
+    // Each thread takes whole 128-row blocks (block b: thread b, b + 1024, ...)
+    // and reads its 128 ids with all loads in flight together (32 16-byte
+    // loads when the ids are 16-byte aligned, else four rounds of 32 4-byte
+    // loads): the block's expert is a maximum in registers, with no
+    // cross-lane steps.
+    const bool aligned16 = ((uintptr_t)p.ids & 15) == 0;
+    for (int b = threadIdx.x; b < nb; b += kRouteThreads) {
+        const int32_t *blk = p.ids + 128 * b;
+        int e = -1;
+        auto take = [&](int x) { e = max(e, (x >= 0 && x < p.G) ? x : -1); };
+        if (aligned16) {
+            int4 v[32];
 #pragma unroll
-        for (int j = 0; j < kDeriveBatch; ++j) {
-            const int b = min(b0 + j, nb - 1);
-            e0[j] = p.ids[128 * b + lane];
-            e1[j] = p.ids[128 * b + 64 + lane];
-        }
+            for (int j = 0; j < 32; ++j)
+                v[j] = reinterpret_cast<const int4 *>(blk)[j];
 #pragma unroll
-        for (int j = 0; j < kDeriveBatch; ++j) {
-            const int a0 = (e0[j] >= 0 && e0[j] < p.G) ? e0[j] : -1;
-            const int a1 = (e1[j] >= 0 && e1[j] < p.G) ? e1[j] : -1;
-            int e = max(a0, a1);
-            for (int o = 32; o > 0; o >>= 1)
-                e = max(e, __shfl_xor(e, o));
-            if (lane == 0 && b0 + j < nb)
-                bexp[b0 + j] = e;
+            for (int j = 0; j < 32; ++j) {
+                take(v[j].x), take(v[j].y), take(v[j].z), take(v[j].w);
+            }
+        } else {
+            for (int r = 0; r < 128; r += 32) {
+                int v[32];
+#pragma unroll
+                for (int j = 0; j < 32; ++j)
+                    v[j] = blk[r + j];
+#pragma unroll
+                for (int j = 0; j < 32; ++j)
+                    take(v[j]);
+            }
         }
+        bexp[b] = e;
     }
     __syncthreads();
     if (w == 0) {

@@ -301,3 +301,27 @@ def test_plain_call_many_experts(gpu_device, G, N, ws):
     assert np.all(got[~valid] == SENTINEL)
     assert_close(got[valid], ref[valid], "G=%d N=%d ws=%s" % (G, N, ws))
     assert np.array_equal(got_tok[tok[valid]], got[valid]), "token order equals the plain call's rows"
+
+
+def test_ids_only_4_byte_aligned(gpu_device):
+    """expert_ids need only 4-byte alignment: ids starting 4 bytes into an
+    allocation (so not 16-byte aligned) give the same rows, bit for bit, as
+    the same ids 16-byte aligned, through the call that derives the segment
+    offsets from them on the device."""
+    G, T, N, K = 6, 1500, 256, 512
+    e = np.random.Generator(np.random.PCG64(990)).choice(G, T).astype(np.int32)
+    c = gen.make_contiguous(G, T, N, K, 991, 992, 0, expert_of_token=e)
+    args = (dev(c.a), dev(c.sa_t).t(), dev(c.b), dev(c.sb))
+    buf = torch.zeros(c.M_total + 1, dtype=torch.int32, device="cuda")
+    buf[1:] = dev(c.ids)
+    ids_off = buf[1:]
+    assert ids_off.data_ptr() % 16 == 4
+    w = ops.workspace(ops.dg_fp8_grouped_gemm_contiguous_workspace_bytes(c.M_total, N, K, G))
+    d0, d1 = sentinel_bf16((c.M_total, N)), sentinel_bf16((c.M_total, N))
+    ops.dg_fp8_grouped_gemm_contiguous_ws(*args, dev(c.ids), w, d=d0)
+    ops.dg_fp8_grouped_gemm_contiguous_ws(*args, ids_off, w, d=d1)
+    torch.cuda.synchronize()
+    assert np.array_equal(bits(d0), bits(d1))
+    ref = oracle.grouped_contiguous(c.a, c.sa_t.T, c.b, c.sb, c.ids, np.full((c.M_total, N), SENTINEL, np.uint16))
+    valid = c.ids >= 0
+    assert_close(bits(d0)[valid], ref[valid], "aligned ids")
