@@ -349,6 +349,27 @@ __device__ inline int tail_split(int tiles, int nk, int max_split, int slots)
     return best;
 }
 
+// Sum of v over the wave's 64 lanes, the same in every lane.
+__device__ __forceinline__ int wave_sum(int v)
+{
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1)
+        v += __shfl_xor(v, o);
+    return __builtin_amdgcn_readfirstlane(v);
+}
+
+// Inclusive prefix sum of v over lanes 0..lane.
+__device__ __forceinline__ int wave_incl_sum(int v, int lane)
+{
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+        const int u = __shfl_up(v, d);
+        if (lane >= d)
+            v += u;
+    }
+    return v;
+}
+
 template <int L, class C, int F = 0, bool SCATTER = false, bool SEG = false>
 __global__ void __launch_bounds__(C::kThreads, 1) tile_kernel(Params p)
 {
@@ -404,14 +425,25 @@ __global__ void __launch_bounds__(C::kThreads, 1) tile_kernel(Params p)
             e = max(e, __shfl_xor(e, o));
         return __builtin_amdgcn_readfirstlane(e);
     };
+    // The segments are read 64 experts at a time, one per lane (a loop over
+    // the experts on the scalar unit would wait for each offset in turn).
+    // Round e0: lane e0 + lane's segment start and size (0 past G).
+    auto seg_of_lane = [&](int e0, int &start, int &size) {
+        const int e = e0 + lane;
+        start = 0;
+        size = 0;
+        if (e < p.G) {
+            start = p.layout[e];
+            size = max(p.layout[e + 1] - start, 0);
+        }
+    };
     int seg_full = 0, seg_half = 0;
     if (SEG && !by_block) {
-        for (int e = 0; e < p.G; ++e) {
-            const int sz = p.layout[e + 1] - p.layout[e];
-            if (sz > 0) {
-                seg_full += sz >> 8;
-                seg_half += (sz >> 7) & 1;
-            }
+        for (int e0 = 0; e0 < p.G; e0 += 64) {
+            int st, sz;
+            seg_of_lane(e0, st, sz);
+            seg_full += wave_sum(sz >> 8);
+            seg_half += wave_sum((sz >> 7) & 1);
         }
     }
     // K slices per work item; segment tails write every slice to the workspace
@@ -444,15 +476,25 @@ __global__ void __launch_bounds__(C::kThreads, 1) tile_kernel(Params p)
             if (ts < seg_full * p.tiles_n) {
                 int ft;
                 tile_coords(ts, seg_full, p.tiles_n, C::kGroupM, ft, nt);
-                int before = 0;  // whole tiles of the experts before seg_e
-                for (seg_e = 0; seg_e < p.G; ++seg_e) {
-                    const int sz = p.layout[seg_e + 1] - p.layout[seg_e];
-                    const int f = sz > 0 ? sz >> 8 : 0;
-                    if (ft < before + f)
+                // the expert whose whole tiles hold tile ft: the first one where
+                // the running count of whole tiles passes ft
+                int before = 0;  // whole tiles of the experts before this round
+                seg_e = -1;
+                for (int e0 = 0; e0 < p.G; e0 += 64) {
+                    int st, sz;
+                    seg_of_lane(e0, st, sz);
+                    const int f = sz >> 8, incl = wave_incl_sum(f, lane);
+                    const uint64_t hit = __ballot(ft < before + incl);
+                    if (hit) {
+                        const int l = (int)__builtin_ctzll(hit);
+                        seg_e = e0 + l;
+                        seg_m0 = __builtin_amdgcn_readfirstlane(__shfl(st + 256 * (ft - before - (incl - f)), l));
                         break;
-                    before += f;
+                    }
+                    before += __builtin_amdgcn_readfirstlane(__shfl(incl, 63));
                 }
-                seg_m0 = p.layout[seg_e] + 256 * (ft - before);
+                if (seg_e < 0)
+                    continue;  // past the segments (uniform over the workgroup)
                 seg_rows = 256;
             } else {
                 const int h = (ts - seg_full * p.tiles_n) / p.tiles_n;
@@ -460,16 +502,28 @@ __global__ void __launch_bounds__(C::kThreads, 1) tile_kernel(Params p)
                     continue;  // past the real tiles (uniform over the workgroup)
                 nt = ts - seg_full * p.tiles_n - h * p.tiles_n;
                 seg_h = h;
+                // the expert of the h-th tail: the h-th segment (in expert
+                // order) whose size is an odd multiple of 128
                 int seen = 0;
-                for (seg_e = 0; seg_e < p.G; ++seg_e) {
-                    const int sz = p.layout[seg_e + 1] - p.layout[seg_e];
-                    if (sz > 0 && ((sz >> 7) & 1)) {
-                        if (seen == h)
-                            break;
-                        ++seen;
+                seg_e = -1;
+                for (int e0 = 0; e0 < p.G; e0 += 64) {
+                    int st, sz;
+                    seg_of_lane(e0, st, sz);
+                    const bool tail = (sz >> 7) & 1;
+                    const uint64_t tails = __ballot(tail);
+                    const int n = __popcll(tails);
+                    if (h < seen + n) {
+                        const int below = __builtin_amdgcn_mbcnt_hi((uint32_t)(tails >> 32),
+                                                                     __builtin_amdgcn_mbcnt_lo((uint32_t)tails, 0));
+                        const int l = (int)__builtin_ctzll(__ballot(tail && below == h - seen));
+                        seg_e = e0 + l;
+                        seg_m0 = __builtin_amdgcn_readfirstlane(__shfl(st + (sz & ~255), l));
+                        break;
                     }
+                    seen += n;
                 }
-                seg_m0 = p.layout[seg_e] + ((p.layout[seg_e + 1] - p.layout[seg_e]) & ~255);
+                if (seg_e < 0)
+                    continue;
                 seg_rows = 128;
             }
             if (seg_m0 < 0 || seg_m0 >= p.M)
@@ -763,21 +817,49 @@ __global__ void __launch_bounds__(C::kThreads, 1) tile_kernel(Params p)
             acc[MI - 1][j] += part[j] * part_sc;
 
         uint16_t *Dg = p.D + (int64_t)g * p.d_stride_g;
-        auto row_ok = [&](int m) {
+        // Contiguous: the expert id (and with SCATTER the token) of each of
+        // this lane's rows, all read before the first store. The compiler
+        // cannot tell the stores from these arrays apart, so a load left
+        // between two rows' stores would wait for the stores' round trip.
+        // Indices are clamped so that every lane loads; bit i of row_bits
+        // says whether this lane's row i is written. (The row numbers are
+        // formed in place: hoisted out of the tile loop, they would be kept
+        // across the K loop.)
+        const int mb = m0 + wm0 + l16;
+        auto row_m = [&](int i) { return (int)add_in_place((uint32_t)mb, 16 * i); };
+        uint32_t row_bits = 0;
+        int row_tok[SCATTER ? MI : 1];
+        if constexpr (L == kContiguous) {
+            int row_id[MI];
+#pragma unroll
+            for (int i = 0; i < MI; ++i) {
+                const int mc = min(row_m(i), p.M - 1);
+                row_id[i] = p.ids[mc];
+                if constexpr (SCATTER)
+                    row_tok[i] = p.row_dst[mc];
+            }
+#pragma unroll
+            for (int i = 0; i < MI; ++i) {
+                // a segment tile covers seg_rows rows (128 for a segment's
+                // tail or a block on its own): the rows after them belong to
+                // another tile, possibly of the same expert
+                const int m = row_m(i);
+                if (m < p.M && (!SEG || m - m0 < seg_rows) && row_id[i] == expert)
+                    row_bits |= 1u << i;
+            }
+        }
+        auto row_ok = [&](int i) {
             if (L == kDense)
-                return m < p.M;
+                return row_m(i) < p.M;
             if (L == kMasked)
-                return m < limit;
-            // a segment tile covers seg_rows rows (128 for a segment's tail
-            // or a block on its own): the rows after them belong to another
-            // tile, possibly of the same expert
-            return m < p.M && (!SEG || m - m0 < seg_rows) && p.ids[m] == expert;
+                return row_m(i) < limit;
+            return ((row_bits >> i) & 1) != 0;
         };
         if (to_ws) {
 #pragma unroll
             for (int i = 0; i < MI; ++i) {
-                const int m = m0 + wm0 + 16 * i + l16;
-                if (!row_ok(m) || (SEG && m - m0 >= seg_rows))
+                const int m = row_m(i);
+                if (!row_ok(i) || (SEG && m - m0 >= seg_rows))
                     continue;
                 // dense: row m of slice `slice`; segment tails: row 128 h + (m - m0)
                 const int64_t wr = SEG ? (int64_t)slice * p.ws_rows + 128 * seg_h + (m - m0)
@@ -794,15 +876,13 @@ __global__ void __launch_bounds__(C::kThreads, 1) tile_kernel(Params p)
             // contiguous kernel spill in its K loop.
 #pragma unroll
             for (int i = 0; i < MI; ++i) {
-                const int m = m0 + wm0 + 16 * i + l16;
-                if (!row_ok(m))
+                if (!row_ok(i))
                     continue;
-                int64_t dm = m;
+                int64_t dm = row_m(i);
                 if constexpr (SCATTER) {  // the row's token: its row of D in token order
-                    const int t = p.row_dst[m];
-                    if (t < 0 || t >= p.dst_rows)
+                    dm = row_tok[i];
+                    if (dm < 0 || dm >= p.dst_rows)
                         continue;
-                    dm = t;
                 }
                 uint16_t *drow = Dg + dm * p.ldd + n0 + wn0 + 4 * lg;
 #pragma unroll
@@ -836,7 +916,7 @@ __global__ void __launch_bounds__(C::kThreads, 1) tile_kernel(Params p)
             const int r = q * RPI + lane / CPR, c = lane % CPR;
             const uint4 v = *reinterpret_cast<const uint4 *>(ep + r * RB + ((c ^ (r & 7)) << 4));
             const int m = m0 + wm0 + r;
-            if (row_ok(m))
+            if (L == kDense ? m < p.M : m < limit)
                 *reinterpret_cast<uint4 *>(Dg + (int64_t)m * p.ldd + n0 + wn0 + c * 8) = v;
         }
         }  // pass
