@@ -134,6 +134,30 @@ def test_to_tokens_with_layout(gpu_device):
     assert_close(bits(out1)[kept], ref, "to tokens with layout")
 
 
+@pytest.mark.parametrize("G,T", [(200, 12000), (1024, 12000)])
+@pytest.mark.parametrize("ws", [True, False])
+def test_layout_many_experts(gpu_device, G, T, ws):
+    """The layout given for hundreds of experts (several rounds of 64 experts
+    in the tiles' segment search, many empty and one-block segments, tails
+    split over K with a workspace): rows of whole tiles equal the uniform grid
+    bit for bit, every valid row matches the oracle, padding stays untouched."""
+    N, K = 256, 640
+    rng = np.random.default_rng(G)
+    # skewed routing: a few large experts among many small or empty ones
+    w = rng.pareto(1.2, G) + 0.05
+    e = rng.choice(G, T, p=w / w.sum()).astype(np.int32)
+    c = gen.make_contiguous(G, T, N, K, 961, 962, 0, expert_of_token=e)
+    layout = layout_of(c.counts)
+    assert layout[-1] == c.M_total
+    grid, seg = run_both(c, layout, ws)
+    valid = c.ids >= 0
+    assert np.all(seg[~valid] == SENTINEL), "padding rows untouched"
+    whole = valid & ~tail_rows(layout, c.M_total)
+    assert np.array_equal(seg[whole], grid[whole]), "whole-tile rows equal the uniform grid"
+    ref = oracle.grouped_contiguous(c.a, c.sa_t.T, c.b, c.sb, c.ids, np.full((c.M_total, N), SENTINEL, np.uint16))
+    assert_close(seg[valid], ref[valid], "layout with G=%d" % G)
+
+
 @pytest.mark.parametrize("kind", ["zeros", "past_the_rows", "negative"])
 @pytest.mark.parametrize("ws", [True, False])
 def test_layout_that_does_not_fit_writes_nothing(gpu_device, kind, ws):
