@@ -15,7 +15,9 @@ the 1x128 activation quantiser and the whole MoE step) is reported under
 
 * timing: the mean over one graph of launches, and median / p10 / p90 over
   at least 100 launches (graphs of 10 launches, each replay timed with HIP
-  events on the launch stream);
+  events on the launch stream); every timed replay follows at least 0.2 s of
+  untimed replays of the same graph, so the GPU runs at the clock it holds
+  under that load;
 * a roofline entry against its bound (MFMA for the large GEMMs, HBM for the
   decode and masked shapes and the quantiser) with the 60% target where one
   is set;
@@ -67,6 +69,8 @@ BOUNDS = {
 }
 NO_BENCH_ORACLE = {"square_4096_e4m3xe5m2"}
 CHUNK = 10          # launches per timed graph replay of the distribution
+WARM_SECONDS = 0.2  # untimed graph replays before each timed one, at least this long
+LAST_WARM_REPLAYS = 0  # untimed replays of the last graph_time call
 MIN_LAUNCHES = 100  # launches timed per workload for the distribution, at least
 
 
@@ -187,8 +191,20 @@ def graph_time(fn, launches, warmup, replays=1):
     with torch.cuda.graph(graph, stream=cap):
         for i in range(launches):
             fn(warmup + i)
-    graph.replay()                  # untimed: the first replay uploads the graph
-    torch.cuda.synchronize()
+    # Untimed replays: the first uploads the graph; the rest run the GPU for
+    # at least WARM_SECONDS so that the timed replays start at the clock it
+    # holds under this load, not at the lower one it drops to while the host
+    # checks the previous workload against the oracle.
+    global LAST_WARM_REPLAYS
+    LAST_WARM_REPLAYS = 0
+    t_warm = time.perf_counter()
+    while True:
+        with torch.cuda.stream(cap):
+            graph.replay()
+        torch.cuda.synchronize()
+        LAST_WARM_REPLAYS += 1
+        if time.perf_counter() - t_warm >= WARM_SECONDS:
+            break
     per_launch, wall = [], None
     for r in range(replays):
         start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -281,11 +297,13 @@ def bench_gemm(name, steps, warmup, check, threads):
         run(i)
     torch.cuda.synchronize()
     per, wall = graph_time(run, steps, 0)
+    warm_replays = LAST_WARM_REPLAYS
     mean_us = per[0]
     dist = distribution(run, 2) if DISTRIBUTION else None
     r = {"kernel_avg_us": round(mean_us, 3), "wall_ms_per_step": round(wall / steps * 1e3, 6),
          "us": dist, "tflops": round(flops / mean_us / 1e6, 2), "gbs": round(byts / mean_us / 1e3, 1),
          "algorithmic_flops": flops, "algorithmic_bytes": byts, "rows": rows, "operand_copies": len(run.copies),
+         "warm_replays": warm_replays,
          "roofline": roofline(name, flops, byts, mean_us), "traffic": load_traffic(name)}
     # The e5m2 oracle sums each block exactly in 128-bit integers, ~50x slower
     # than the e4m3 one: the whole 4096^3 problem takes minutes, so that
@@ -526,6 +544,7 @@ def main():
                        rhs_scale="128x128", operand_copies=head["operand_copies"]),
         "tflops": head["tflops"],
         "us": head["us"],
+        "warm_replays": head["warm_replays"],
         "roofline": roof,
         "cpu_baseline": cpu,
         "parity": head.get("parity"),
