@@ -58,6 +58,49 @@ def test_mfma_full_code_range(gpu_device):
         assert_close(run_dense(a[:m_rows], sa[:m_rows], b, sb), ref[:m_rows], "full code range")
 
 
+def test_mfma_partial_against_exact_int64(gpu_device):
+    """One K block through one FP8 MFMA against its exact value. A 128x128
+    output split over its 8 K blocks (the split-K path, one block per slice)
+    with unit scales leaves each block's fp32 MFMA partial in the caller's
+    workspace ([slice][M][N] fp32, the promotion multiplying by 1). Each is
+    compared with the exact sum, an int64 dot product of the codes' integer
+    values (2^9 dec(code)) over 2^18. The error is measured against the sum of
+    the terms' magnitudes, the scale an accumulation error has, and printed
+    with the effective bits it leaves: the instruction does not accumulate
+    its 128 products exactly (a few 1e-4 of the terms' magnitude), which is
+    why each 128-wide block's partial is promoted into the fp32 accumulator
+    on its own instead of being accumulated further inside the MFMA."""
+    rng = np.random.default_rng(77)
+    finite = np.array([c for c in range(256) if c not in (0x7F, 0xFF)], np.uint8)
+    M = N = 128
+    K = 1024
+    a = rng.choice(finite, (M, K))
+    b = rng.choice(finite, (N, K))
+    sa = np.ones((M, K // 128), np.float32)
+    sb = np.ones((N // 128, K // 128), np.float32)
+    nbytes = ops.dg_fp8_gemm_nt_workspace_bytes(M, N, K)
+    ks = nbytes // (M * N * 4)
+    assert ks == K // 128, "expected one K block per slice (%d slices)" % ks
+    w = ops.workspace(nbytes)
+    d = sentinel_bf16((M, N))
+    ops.dg_fp8_gemm_nt_ws(dev(a), dev(np.ascontiguousarray(sa.T)).t(), dev(b), dev(sb), w, d=d)
+    torch.cuda.synchronize()
+    part = w[:ks * M * N * 4].view(torch.float32).cpu().numpy().reshape(ks, M, N).astype(np.float64)
+    dec = np.array([oracle.e4m3_decode(c) if c not in (0x7F, 0xFF) else 0.0 for c in range(256)])
+    ia = np.rint(dec[a] * 512).astype(np.int64)
+    ib = np.rint(dec[b] * 512).astype(np.int64)
+    worst = 0.0
+    for s in range(ks):
+        blk = slice(128 * s, 128 * s + 128)
+        ex = (ia[:, blk] @ ib[:, blk].T).astype(np.float64) / 2.0 ** 18
+        mag = (np.abs(ia[:, blk]) @ np.abs(ib[:, blk]).T).astype(np.float64) / 2.0 ** 18
+        worst = max(worst, float((np.abs(part[s] - ex) / mag).max()))
+    print("MFMA fp32 partial vs exact: max error %.3g of the terms' magnitude (%.1f bits)"
+          % (worst, -np.log2(worst) if worst > 0 else float("inf")))
+    assert worst <= 2.0 ** -10
+    assert_close(bits(d), oracle.gemm_nt(a, sa, b, sb), "split-K partial test output")
+
+
 def test_identity_rhs(gpu_device):
     p = gen.make_dense(100, 256, 256, 41, 42)
     b = np.zeros((256, 256), np.uint8)
